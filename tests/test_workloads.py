@@ -1,0 +1,88 @@
+"""The seeded generator and the work counts that price a launch."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import allowed_matrix
+from sliding_window_gqa_varlen_amd import metrics, workloads as W
+
+
+def test_document_lengths_for_the_five_workloads():
+    assert W.dense_doc_lengths(W.WORKLOADS[0]) == [5, 17, 42]
+    assert W.dense_doc_lengths(W.WORKLOADS[1]) == [1036, 1111, 1578, 1953, 194, 404, 1708, 208]
+    assert W.dense_doc_lengths(W.WORKLOADS[2]) == [6945, 2521, 1351, 2804, 3690, 6766, 3978, 1218, 3084, 411]
+    d3 = W.dense_doc_lengths(W.WORKLOADS[3])
+    assert len(d3) == 27 and sum(d3) == 65536 and d3[:5] == [103, 238, 5443, 1615, 108]
+    assert W.sparse_doc_lengths(W.WORKLOADS[4]) == [6231, 7784, 2369]
+    for w in W.WORKLOADS[1:4]:
+        assert sum(W.dense_doc_lengths(w)) == w.T
+
+
+def test_mask_effective_pair_counts():
+    pairs = [metrics.dense_allowed_pairs(W.dense_doc_lengths(w), w.window) for w in W.WORKLOADS[:4]]
+    assert pairs == [1071, 5890741, 28504250, 8171794]
+    assert metrics.sparse_generated_slots(W.sparse_doc_lengths(W.WORKLOADS[4]), 2048) == 27266048
+
+
+@pytest.mark.parametrize("window", [0, 1, 3, 7, 50])
+def test_pair_count_matches_the_brute_force_mask(window):
+    lengths = [4, 0, 13, 1, 9]
+    cu = W.cu_seqlens_from_lengths(lengths)
+    A = allowed_matrix(cu, sum(lengths) + 2, window)
+    assert int(A.sum()) == metrics.dense_allowed_pairs(lengths, window)
+
+
+def test_bf16_rounding_matches_torch_round_to_nearest_even():
+    rng = np.random.default_rng(0)
+    x = np.concatenate([rng.standard_normal(100000).astype(np.float32) * 10.0 ** rng.integers(-6, 6, 100000),
+                        np.array([1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -1.0 - 2 ** -8, 65504.0, 3.0e38], np.float32)])
+    ours = W.round_to_bf16(x.copy())
+    ref = torch.from_numpy(x.copy()).to(torch.bfloat16).to(torch.float32).numpy()
+    np.testing.assert_array_equal(ours, ref)
+    # ties go to even
+    assert W.round_to_bf16(np.array([1.0 + 2 ** -8], np.float32))[0] == 1.0
+    assert W.round_to_bf16(np.array([1.0 + 3 * 2 ** -8], np.float32))[0] == 1.0 + 2 ** -6
+
+
+def test_chunked_draws_equal_one_shot_draws():
+    a = W.normal(3, W.STREAM_Q, (70000, 300))
+    b = np.random.default_rng([3, W.STREAM_Q]).standard_normal((70000, 300), dtype=np.float32)
+    np.testing.assert_array_equal(a, b)
+
+
+def test_dense_inputs_shapes_and_rounding():
+    w = W.WORKLOADS[3].with_tokens(2048)
+    inp = W.make_dense(w)
+    assert inp["q"].shape == (2048, 64, 64) and inp["k"].shape == (2048, 8, 64)
+    assert inp["sinks"].dtype == np.float32 and inp["sinks"].shape == (64,)
+    for name in ("q", "k", "v"):
+        x = inp[name]
+        np.testing.assert_array_equal(W.round_to_bf16(x.copy()), x)
+    assert inp["cu_seqlens"][-1] == 2048 and inp["cu_seqlens"].dtype == np.int32
+
+
+def test_rms_normalised_queries_have_unit_rms_before_rounding():
+    w = W.WORKLOADS[2].with_tokens(1024)
+    q = W.scaleless_rms_norm(W.normal(w.seed, W.STREAM_Q, (1024, 32, 128)))
+    rms = np.sqrt((q.astype(np.float64) ** 2).mean(-1))
+    np.testing.assert_allclose(rms, 1.0, atol=1e-4)
+
+
+def test_sparse_indices_are_causal_same_document_sorted_distinct():
+    w = W.WORKLOADS[4].with_tokens(3000, topk=256)
+    lengths = W.sparse_doc_lengths(w)
+    idx = W.make_sparse_indices(w.seed, lengths, w.T, w.topk)
+    ids = W.doc_ids_from_lengths(w.T, lengths)
+    start = 0
+    for L in lengths:
+        for p in range(L):
+            t = start + p
+            row = idx[t]
+            n = int((row >= 0).sum())
+            assert n == min(p + 1, w.topk)
+            assert np.all(row[n:] == -1)
+            sel = row[:n]
+            assert np.all(np.diff(sel) > 0)
+            assert sel[0] >= start and sel[-1] <= t
+        start += L
+    assert metrics.sparse_valid_slots(idx, ids) == metrics.sparse_generated_slots(lengths, w.topk)
