@@ -1,0 +1,156 @@
+/*
+ * swattn.h — C ABI of libswattn.so: forward attention over packed variable-length
+ * (THD) token streams on MI355X (gfx950).
+ *
+ * Two operations:
+ *
+ *  varlen_attn_fwd  Causal or causal sliding-window GQA attention over documents
+ *                   packed back to back and delimited by cu_seqlens, with a score
+ *                   scale and an optional learned per-query-head sink logit.
+ *                   Defined by MuseMagiPlan.attention (query/key/value/window/scale;
+ *                   nemo_automodel.components.models.muse_spark.magi_cp page),
+ *                   FlintMagiPlan.attention (sink; window counts the current token;
+ *                   nemo_automodel.components.models.flint.magi page), the GQA head
+ *                   grouping of MuseGlimmerAttention / repeat_kv
+ *                   (nemo_automodel.components.models.muse_glimmer.model page) and
+ *                   the causal document mask of SequenceLayout.allowed
+ *                   (nemo_automodel.components.models.mistral_large4.attention page).
+ *
+ *  sparse_mla_fwd   Sparse MLA forward: each query token attends to the top-k key
+ *                   rows its index row names; a key is a shared 512-wide latent row
+ *                   plus a 64-wide rotary row and the value is the latent row.
+ *                   Defined by sparse_mla and MistralLarge4Attention._sparse_forward
+ *                   (nemo_automodel.components.models.mistral_large4.attention page).
+ *
+ * Conventions common to every entry point
+ *  - Tensors are described by swa_tensor: a device pointer plus shape and strides in
+ *    elements. The innermost dimension must be contiguous (stride 1); the other
+ *    strides are free but must keep every row 16-byte aligned (base pointer and
+ *    row strides multiples of 16 bytes).
+ *  - The caller allocates and owns every buffer. The library allocates no device
+ *    memory, keeps no per-call state and performs no host<->device copy or
+ *    synchronisation: a call validates its arguments on the host, enqueues its
+ *    kernels on `stream` (a hipStream_t; NULL = the legacy default stream) and
+ *    returns. Buffers must stay valid until that stream work completes.
+ *  - Outputs must not alias inputs.
+ *  - Return value: SWA_OK (0) or a negative swa_status. On any error detected on the
+ *    host nothing is enqueued and the outputs are untouched; swa_last_error() then
+ *    names the offending argument. No C++ exception crosses this interface.
+ *  - Contract violations that only the device can see (non-monotone cu_seqlens,
+ *    out-of-range indices) never cause an out-of-bounds access: offsets are
+ *    clamped to [0, T] and out-of-range indices act as empty slots. The values
+ *    written for tokens of a malformed cu_seqlens are then unspecified.
+ *  - Thread-safe and reentrant; calls on different streams may run concurrently.
+ */
+#ifndef SWATTN_H_
+#define SWATTN_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SWA_ABI_VERSION 1
+
+/* Element types of swa_tensor.dtype. */
+enum swa_dtype {
+  SWA_DTYPE_F32 = 0,  /* IEEE binary32 */
+  SWA_DTYPE_BF16 = 1, /* bfloat16 */
+  SWA_DTYPE_I32 = 2   /* int32 */
+};
+
+/* Status codes. */
+enum swa_status {
+  SWA_OK = 0,
+  SWA_ERR_NULL = -1,        /* a required pointer is NULL */
+  SWA_ERR_DTYPE = -2,       /* unsupported or mismatched element type */
+  SWA_ERR_SHAPE = -3,       /* ranks or shapes disagree */
+  SWA_ERR_ARG = -4,         /* a scalar argument is out of range */
+  SWA_ERR_UNSUPPORTED = -5, /* well-formed but not implemented (e.g. head_dim) */
+  SWA_ERR_LAYOUT = -6,      /* stride or alignment requirement violated */
+  SWA_ERR_LAUNCH = -7       /* the HIP runtime rejected the launch */
+};
+
+/* Non-owning view of a device tensor of rank <= 3. */
+typedef struct swa_tensor {
+  void* data;        /* device pointer (may be NULL only when the tensor is empty) */
+  int32_t dtype;     /* enum swa_dtype */
+  int32_t ndim;      /* number of valid entries in shape[] and stride[] */
+  int64_t shape[3];
+  int64_t stride[3]; /* in elements; stride[ndim-1] must be 1 */
+} swa_tensor;
+
+/*
+ * varlen_attn_fwd — packed varlen causal / sliding-window GQA attention forward.
+ *
+ * For every document d = [cu_seqlens[d], cu_seqlens[d+1]), every token i in it and
+ * every query head h (KV head g = h / (Hq/Hkv)):
+ *     allowed(i,j)  <=>  cu_seqlens[d] <= j <= i  and  (window == 0 or i - j < window)
+ *     S_j = scale * <q[i,h,:], k[j,g,:]>
+ *     Z   = sum_{allowed j} exp(S_j)  +  exp(sinks[h])        (sink term only if sinks)
+ *     out[i,h,:] = sum_{allowed j} exp(S_j) * v[j,g,:] / Z ;  lse[i,h] = ln Z
+ * The sink is a logit: it is not multiplied by scale and has no value vector.
+ * Tokens outside every document (before cu_seqlens[0] or from cu_seqlens[n_docs]
+ * to T) are padding: out = 0, lse = -inf.
+ *
+ *   q          [T, Hq, D]   bf16 or f32
+ *   k, v       [T, Hkv, D]  same dtype as q; Hq must be a multiple of Hkv
+ *   cu_seqlens device int32 [n_docs + 1], non-decreasing document offsets with
+ *              cu_seqlens[n_docs] <= T (zero-length documents allowed); may be
+ *              NULL when n_docs == 0 (every token is padding)
+ *   n_docs     >= 0
+ *   window     >= 0; 0 = full causal, else the key window length including the
+ *              current token
+ *   scale      finite and > 0
+ *   sinks      device f32 [Hq] learned logits, or NULL for none (-inf = no sink)
+ *   out        [T, Hq, D]  same dtype as q
+ *   lse        device f32 [T, Hq] contiguous (natural log), or NULL
+ *   stream     hipStream_t
+ * Supported: D in {64, 128}. Arithmetic: f32 accumulation; bf16 inputs use bf16
+ * matrix products with the probabilities rounded to bf16 for the value product,
+ * and the output is rounded once from f32.
+ */
+int32_t varlen_attn_fwd(const swa_tensor* q, const swa_tensor* k, const swa_tensor* v,
+                        const int32_t* cu_seqlens, int32_t n_docs, int32_t window, float scale,
+                        const float* sinks, swa_tensor* out, float* lse, void* stream);
+
+/*
+ * sparse_mla_fwd — sparse MLA forward over gathered top-k latent rows.
+ *
+ * For token t, head h and slot r of indices[t,:] (idx = indices[t,r]):
+ *     valid(r)  <=>  0 <= idx < T  and  idx <= t  and  doc_ids[idx] == doc_ids[t] >= 0
+ *     S_r = scale * (<q[t,h,:Dl], latent[idx,:]> + <q[t,h,Dl:], k_pe[idx,:]>)
+ *     out[t,h,:] = sum_{valid r} softmax(S)_r * latent[idx,:] ;  lse[t,h] = ln sum exp(S_r)
+ * -1 marks an empty slot; repeated indices count once per slot; a row with no
+ * valid slot gives out = 0 and lse = -inf. The value is the latent row (the KV-B
+ * value up-projection is not part of this call).
+ *
+ *   q        [T, H, Dl + Dr] bf16, latent coordinates first, rotary last
+ *   latent   [T, Dl] bf16
+ *   k_pe     [T, Dr] bf16
+ *   indices  [T, topk] int32, topk >= 1
+ *   doc_ids  device int32 [T] document id per token (< 0 = padding token)
+ *   scale    finite and > 0
+ *   out      [T, H, Dl] bf16
+ *   lse      device f32 [T, H] contiguous, or NULL
+ * Supported: Dl = 512, Dr = 64, H a multiple of 16.
+ */
+int32_t sparse_mla_fwd(const swa_tensor* q, const swa_tensor* latent, const swa_tensor* k_pe,
+                       const swa_tensor* indices, const int32_t* doc_ids, float scale,
+                       swa_tensor* out, float* lse, void* stream);
+
+/* Static description of a status code. Never NULL. */
+const char* swa_strerror(int32_t status);
+
+/* Detail of the last failing call on the calling thread ("" if none). Never NULL. */
+const char* swa_last_error(void);
+
+/* SWA_ABI_VERSION of the loaded library. */
+int32_t swa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SWATTN_H_ */

@@ -1,0 +1,168 @@
+"""ctypes binding of libswattn.so (argument marshalling only).
+
+The functions here turn torch tensors into ``swa_tensor`` descriptors, pick the
+current HIP stream and call the C entry points of the same name.  No step of
+the attention runs here; if the library is missing or a call fails, they
+raise — there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import threading
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libswattn.so"
+_lock = threading.Lock()
+_lib = None
+
+SWA_DTYPE_F32, SWA_DTYPE_BF16, SWA_DTYPE_I32 = 0, 1, 2
+_DTYPES = {torch.float32: SWA_DTYPE_F32, torch.bfloat16: SWA_DTYPE_BF16, torch.int32: SWA_DTYPE_I32}
+
+# functions the header declares, with their ctypes signatures
+EXPORTS = ("varlen_attn_fwd", "sparse_mla_fwd", "swa_strerror", "swa_last_error", "swa_abi_version")
+
+
+class SwaTensor(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("ndim", ctypes.c_int32),
+                ("shape", ctypes.c_int64 * 3), ("stride", ctypes.c_int64 * 3)]
+
+
+class SwaError(RuntimeError):
+    def __init__(self, fn: str, status: int, detail: str, text: str):
+        super().__init__(f"{fn} failed with status {status} ({text}): {detail}")
+        self.status = status
+
+
+def library_path() -> str:
+    return os.environ.get("SWATTN_LIB", os.path.join(_HERE, _LIB_NAME))
+
+
+def load_library():
+    """Load libswattn.so once; raise if it was not built."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        path = library_path()
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} not found: build it with `python -m sliding_window_gqa_varlen_amd.build`")
+        lib = ctypes.CDLL(path)
+        P = ctypes.POINTER(SwaTensor)
+        vp, i32, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
+        lib.varlen_attn_fwd.argtypes = [P, P, P, vp, i32, i32, f32, vp, P, vp, vp]
+        lib.varlen_attn_fwd.restype = i32
+        lib.sparse_mla_fwd.argtypes = [P, P, P, P, vp, f32, P, vp, vp]
+        lib.sparse_mla_fwd.restype = i32
+        lib.swa_strerror.argtypes = [i32]
+        lib.swa_strerror.restype = ctypes.c_char_p
+        lib.swa_last_error.argtypes = []
+        lib.swa_last_error.restype = ctypes.c_char_p
+        lib.swa_abi_version.argtypes = []
+        lib.swa_abi_version.restype = i32
+        _lib = lib
+        return lib
+
+
+def describe(t: Optional[torch.Tensor]) -> Optional[SwaTensor]:
+    """swa_tensor view of a torch tensor (rank <= 3; strides in elements)."""
+    if t is None:
+        return None
+    if t.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    if t.dim() > 3:
+        raise ValueError("rank > 3")
+    d = SwaTensor()
+    d.data = t.data_ptr() if t.numel() > 0 else None
+    d.dtype = _DTYPES[t.dtype]
+    d.ndim = t.dim()
+    for i in range(t.dim()):
+        d.shape[i] = t.shape[i]
+        d.stride[i] = t.stride(i)
+    return d
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        lib = load_library()
+        raise SwaError(fn, status, lib.swa_last_error().decode(), lib.swa_strerror(status).decode())
+
+
+def varlen_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: Optional[torch.Tensor],
+                    n_docs: Optional[int] = None, window: int = 0, scale: Optional[float] = None,
+                    sinks: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                    lse: Optional[torch.Tensor] = None, stream=None, return_lse: bool = True):
+    """Packed varlen causal / sliding-window GQA attention forward on the GPU.
+
+    q [T, Hq, D], k/v [T, Hkv, D] (bf16 or f32, on the GPU); cu_seqlens int32
+    [n_docs + 1] on the GPU; window 0 = full causal; scale defaults to
+    D ** -0.5; sinks optional fp32 [Hq].  Returns (out, lse) — lse is None when
+    ``return_lse`` is False and no ``lse`` buffer is given.
+    """
+    lib = load_library()
+    T, Hq, D = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if n_docs is None:
+        n_docs = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
+    if out is None:
+        out = torch.empty((T, Hq, D), dtype=q.dtype, device=q.device)
+    if lse is None and return_lse:
+        lse = torch.empty((T, Hq), dtype=torch.float32, device=q.device)
+    if cu_seqlens is not None and cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    if sinks is not None and sinks.dtype != torch.float32:
+        raise TypeError("sinks must be float32")
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != (T, Hq)):
+        raise ValueError("lse must be a contiguous float32 [T, Hq] tensor")
+    dq, dk, dv, do = describe(q), describe(k), describe(v), describe(out)
+    st = lib.varlen_attn_fwd(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), _ptr(cu_seqlens),
+                             int(n_docs), int(window), float(scale), _ptr(sinks), ctypes.byref(do),
+                             _ptr(lse), _stream(stream))
+    _check("varlen_attn_fwd", st)
+    return out, lse
+
+
+def sparse_mla_fwd(q: torch.Tensor, latent: torch.Tensor, k_pe: torch.Tensor, indices: torch.Tensor,
+                   doc_ids: torch.Tensor, scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                   lse: Optional[torch.Tensor] = None, stream=None, return_lse: bool = True):
+    """Sparse MLA forward: gathered top-k latent (512) + rotary (64) keys, value = latent.
+
+    q [T, H, 576] bf16, latent [T, 512] bf16, k_pe [T, 64] bf16, indices int32
+    [T, topk] (-1 = empty slot), doc_ids int32 [T]; scale defaults to 576 ** -0.5.
+    Returns (out [T, H, 512] bf16, lse [T, H] fp32 or None).
+    """
+    lib = load_library()
+    T, H, Dqk = q.shape
+    Dl = latent.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(Dqk)
+    if out is None:
+        out = torch.empty((T, H, Dl), dtype=q.dtype, device=q.device)
+    if lse is None and return_lse:
+        lse = torch.empty((T, H), dtype=torch.float32, device=q.device)
+    if doc_ids.dtype != torch.int32:
+        raise TypeError("doc_ids must be int32")
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != (T, H)):
+        raise ValueError("lse must be a contiguous float32 [T, H] tensor")
+    dq, dl, dr, di, do = describe(q), describe(latent), describe(k_pe), describe(indices), describe(out)
+    st = lib.sparse_mla_fwd(ctypes.byref(dq), ctypes.byref(dl), ctypes.byref(dr), ctypes.byref(di),
+                            _ptr(doc_ids), float(scale), ctypes.byref(do), _ptr(lse), _stream(stream))
+    _check("sparse_mla_fwd", st)
+    return out, lse

@@ -1,0 +1,56 @@
+// Internal interface between the C ABI layer (abi.cpp) and the kernel launchers.
+#pragma once
+
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+namespace swa {
+
+// Packed varlen GQA forward. All strides in elements.
+struct DenseFwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;
+  int64_t q_st, q_sh, k_st, k_sh, v_st, v_sh, o_st, o_sh;  // token / head strides
+  const int32_t* cu_seqlens;                              // device [n_docs + 1] or null
+  const float* sinks;                                     // device [Hq] or null
+  float* lse;                                             // device [T, Hq] or null
+  int32_t T, n_docs, Hq, Hkv, G;
+  int32_t hb_shift;     // log2 of the query heads folded into one wave's 32 columns
+  int32_t n_chunks;     // G >> hb_shift head chunks per KV head
+  int32_t tile_tokens;  // tokens per workgroup = 128 >> hb_shift
+  int32_t n_vtiles;     // virtual query tiles per (KV head, chunk)
+  int32_t n_work;       // Hkv * n_chunks * n_vtiles
+  int32_t window;
+  float scale;
+  float c2;             // scale * log2(e)
+};
+
+enum class Dtype : int32_t { F32 = 0, BF16 = 1 };
+
+// Grid size (workgroups) the dense launcher will use; 0 when there is no work.
+int64_t dense_fwd_grid(const DenseFwdParams& p);
+// Fills the derived fields of p (hb_shift ... c2) from the user-facing ones.
+void dense_fwd_plan(DenseFwdParams& p);
+hipError_t dense_fwd_launch(const DenseFwdParams& p, Dtype dt, int D, hipStream_t stream);
+
+// Sparse MLA forward (bf16). Strides in elements.
+struct SparseMlaParams {
+  const void* q;       // [T, H, 576]
+  const void* latent;  // [T, 512]
+  const void* k_pe;    // [T, 64]
+  const int32_t* indices;  // [T, topk]
+  const int32_t* doc_ids;  // [T]
+  void* out;           // [T, H, 512]
+  float* lse;          // [T, H] or null
+  int64_t q_st, q_sh, lat_st, kpe_st, idx_st, o_st, o_sh;
+  int32_t T, H, topk;
+  float scale;
+  float c2;
+};
+
+hipError_t sparse_mla_fwd_launch(const SparseMlaParams& p, hipStream_t stream);
+
+}  // namespace swa

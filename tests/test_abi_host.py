@@ -1,0 +1,177 @@
+"""The C ABI on the host: the library loads, exports what include/swattn.h declares,
+and rejects every malformed call before touching the GPU (no compute call here)."""
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import pytest
+import torch
+
+from sliding_window_gqa_varlen_amd import binding
+from sliding_window_gqa_varlen_amd.binding import SwaError, describe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "swattn.h")
+
+SWA_OK, SWA_ERR_NULL, SWA_ERR_DTYPE, SWA_ERR_SHAPE, SWA_ERR_ARG, SWA_ERR_UNSUPPORTED, SWA_ERR_LAYOUT = \
+    0, -1, -2, -3, -4, -5, -6
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_expected_entry_points():
+    assert declared_functions() == sorted(binding.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", binding.library_path()], capture_output=True, text=True)
+    exported = {line.split()[-1] for line in out.stdout.splitlines() if " T " in line}
+    for name in declared_functions():
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+
+
+def test_version_and_error_strings(lib):
+    assert lib.swa_abi_version() == 1
+    for code in (0, -1, -2, -3, -4, -5, -6, -7, 12345):
+        assert len(lib.swa_strerror(code)) > 0
+    assert lib.swa_strerror(0) == b"success"
+
+
+# ---------------------------------------------------------------- dense argument checks
+def dense_args(T=16, Hq=4, Hkv=2, D=64, dtype=torch.bfloat16):
+    q = torch.zeros(T, Hq, D, dtype=dtype)
+    k = torch.zeros(T, Hkv, D, dtype=dtype)
+    v = torch.zeros(T, Hkv, D, dtype=dtype)
+    out = torch.zeros(T, Hq, D, dtype=dtype)
+    cu = torch.tensor([0, T], dtype=torch.int32)
+    return dict(q=q, k=k, v=v, out=out, cu=cu)
+
+
+def call_dense(lib, a, n_docs=1, window=0, scale=0.125, sinks=None, lse=None, descs=None, cu="default"):
+    d = descs or {n: describe(a[n]) for n in ("q", "k", "v", "out")}
+    ref = lambda x: None if x is None else ctypes.byref(x)  # noqa: E731
+    cu_ptr = ctypes.c_void_p(a["cu"].data_ptr()) if cu == "default" else cu
+    return lib.varlen_attn_fwd(ref(d["q"]), ref(d["k"]), ref(d["v"]), cu_ptr, n_docs, window, scale,
+                               sinks, ref(d["out"]), lse, None)
+
+
+def test_dense_rejects_null_descriptors(lib):
+    a = dense_args()
+    for name in ("q", "k", "v", "out"):
+        d = {n: describe(a[n]) for n in ("q", "k", "v", "out")}
+        d[name] = None
+        assert call_dense(lib, a, descs=d) == SWA_ERR_NULL
+        assert name in lib.swa_last_error().decode()
+
+
+def test_dense_rejects_null_cu_seqlens_with_documents(lib):
+    assert call_dense(lib, dense_args(), cu=None) == SWA_ERR_NULL
+
+
+def test_dense_rejects_bad_ranks_shapes_and_dtypes(lib):
+    a = dense_args()
+    d = {n: describe(a[n]) for n in ("q", "k", "v", "out")}
+    d["q"].ndim = 2
+    assert call_dense(lib, a, descs=d) == SWA_ERR_SHAPE
+    b = dense_args()
+    b["k"] = torch.zeros(15, 2, 64, dtype=torch.bfloat16)
+    assert call_dense(lib, b) == SWA_ERR_SHAPE
+    b = dense_args(Hq=3, Hkv=2)
+    assert call_dense(lib, b) == SWA_ERR_SHAPE
+    assert "multiple" in lib.swa_last_error().decode()
+    b = dense_args()
+    b["out"] = torch.zeros(16, 4, 64, dtype=torch.float32)
+    assert call_dense(lib, b) == SWA_ERR_DTYPE
+    b = dense_args(dtype=torch.int32)
+    assert call_dense(lib, b) == SWA_ERR_DTYPE
+    b = dense_args()
+    b["v"] = torch.zeros(16, 2, 128, dtype=torch.bfloat16)
+    assert call_dense(lib, b) == SWA_ERR_SHAPE
+
+
+@pytest.mark.parametrize("D", [32, 96, 256])
+def test_dense_rejects_unsupported_head_dim(lib, D):
+    assert call_dense(lib, dense_args(D=D)) == SWA_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(window=-1), SWA_ERR_ARG), (dict(n_docs=-1), SWA_ERR_ARG), (dict(scale=0.0), SWA_ERR_ARG),
+    (dict(scale=-0.5), SWA_ERR_ARG), (dict(scale=math.nan), SWA_ERR_ARG), (dict(scale=math.inf), SWA_ERR_ARG)])
+def test_dense_rejects_bad_scalars(lib, kw, code):
+    assert call_dense(lib, dense_args(), **kw) == code
+
+
+def test_dense_rejects_misaligned_or_strided_layouts(lib):
+    a = dense_args()
+    base = torch.zeros(16 * 4 * 64 + 1, dtype=torch.bfloat16)
+    a["q"] = base[1:].view(16, 4, 64)  # 2-byte offset: not 16-byte aligned
+    assert call_dense(lib, a) == SWA_ERR_LAYOUT
+    a = dense_args()
+    a["k"] = torch.zeros(16, 2, 128, dtype=torch.bfloat16)[:, :, ::2]  # innermost stride 2
+    assert call_dense(lib, a) == SWA_ERR_LAYOUT
+    a = dense_args()
+    a["v"] = torch.zeros(16, 2, 68, dtype=torch.bfloat16)[:, :, :64]  # row stride 136 bytes
+    assert call_dense(lib, a) == SWA_ERR_LAYOUT
+
+
+def test_dense_rejects_output_aliasing_an_input(lib):
+    a = dense_args(Hq=2, Hkv=2)
+    a["out"] = a["q"]
+    assert call_dense(lib, a) == SWA_ERR_ARG
+
+
+def test_dense_empty_problem_is_a_no_op(lib):
+    a = dense_args(T=0)
+    assert call_dense(lib, a, n_docs=0) == SWA_OK
+
+
+def test_binding_raises_with_the_library_detail(lib):
+    a = dense_args()
+    with pytest.raises(SwaError, match="window"):
+        binding.varlen_attn_fwd(a["q"], a["k"], a["v"], a["cu"], window=-3, stream=0)
+
+
+# ---------------------------------------------------------------- sparse argument checks
+def sparse_args(T=8, H=16, topk=4):
+    return dict(q=torch.zeros(T, H, 576, dtype=torch.bfloat16), latent=torch.zeros(T, 512, dtype=torch.bfloat16),
+                k_pe=torch.zeros(T, 64, dtype=torch.bfloat16), idx=torch.zeros(T, topk, dtype=torch.int32),
+                ids=torch.zeros(T, dtype=torch.int32), out=torch.zeros(T, H, 512, dtype=torch.bfloat16))
+
+
+def call_sparse(lib, a, scale=0.05, ids="default"):
+    d = {n: describe(a[n]) for n in ("q", "latent", "k_pe", "idx", "out")}
+    ids_ptr = ctypes.c_void_p(a["ids"].data_ptr()) if ids == "default" else ids
+    return lib.sparse_mla_fwd(ctypes.byref(d["q"]), ctypes.byref(d["latent"]), ctypes.byref(d["k_pe"]),
+                              ctypes.byref(d["idx"]), ids_ptr, scale, ctypes.byref(d["out"]), None, None)
+
+
+def test_sparse_rejects_bad_arguments(lib):
+    assert call_sparse(lib, sparse_args(), ids=None) == SWA_ERR_NULL
+    a = sparse_args()
+    a["idx"] = torch.zeros(8, 4, dtype=torch.float32)
+    assert call_sparse(lib, a) == SWA_ERR_DTYPE
+    a = sparse_args()
+    a["q"] = torch.zeros(8, 16, 512, dtype=torch.bfloat16)
+    assert call_sparse(lib, a) == SWA_ERR_SHAPE
+    a = sparse_args(H=12)
+    assert call_sparse(lib, a) == SWA_ERR_UNSUPPORTED
+    a = sparse_args(topk=0)
+    assert call_sparse(lib, a) == SWA_ERR_ARG
+    assert call_sparse(lib, sparse_args(), scale=-1.0) == SWA_ERR_ARG
+    a = sparse_args()
+    a["out"] = torch.zeros(8, 16, 512, dtype=torch.float32)
+    assert call_sparse(lib, a) == SWA_ERR_DTYPE
+    a = sparse_args()
+    a["latent"] = torch.zeros(8, 256, dtype=torch.bfloat16)
+    assert call_sparse(lib, a) == SWA_ERR_SHAPE
+
+
+def test_sparse_empty_problem_is_a_no_op(lib):
+    assert call_sparse(lib, sparse_args(T=0)) == SWA_OK
