@@ -26,7 +26,8 @@
  *  - Tensors are described by swa_tensor: a device pointer plus shape and strides in
  *    elements. The innermost dimension must be contiguous (stride 1); the other
  *    strides are free but must keep every row 16-byte aligned (base pointer and
- *    row strides multiples of 16 bytes).
+ *    row strides multiples of 16 bytes) — except sparse_mla_fwd's int32 indices,
+ *    whose rows need only 4-byte alignment.
  *  - The caller allocates and owns every buffer. The library allocates no device
  *    memory, keeps no per-call state and performs no host<->device copy or
  *    synchronisation: a call validates its arguments on the host, enqueues its

@@ -34,7 +34,9 @@ int elem_size(int32_t dtype) {
 }
 
 // Shape/stride/alignment checks shared by every tensor argument.
-int32_t check_tensor(const swa_tensor* t, const char* name, int ndim, bool allow_null_data_if_empty = true) {
+// `row_align` is the byte alignment every row (and the base pointer) must keep: 16 for
+// tensors the kernels read in 16-byte vectors, 4 for the index rows read element-wise.
+int32_t check_tensor(const swa_tensor* t, const char* name, int ndim, int row_align = 16) {
   if (t == nullptr) return fail(SWA_ERR_NULL, "%s: descriptor is NULL", name);
   if (t->ndim != ndim) return fail(SWA_ERR_SHAPE, "%s: expected rank %d, got %d", name, ndim, t->ndim);
   int64_t numel = 1;
@@ -44,17 +46,15 @@ int32_t check_tensor(const swa_tensor* t, const char* name, int ndim, bool allow
   }
   const int es = elem_size(t->dtype);
   if (es == 0) return fail(SWA_ERR_DTYPE, "%s: unknown dtype %d", name, t->dtype);
-  if (numel == 0) {
-    if (t->data == nullptr && allow_null_data_if_empty) return SWA_OK;
-  }
+  if (numel == 0 && t->data == nullptr) return SWA_OK;
   if (t->data == nullptr) return fail(SWA_ERR_NULL, "%s: data pointer is NULL", name);
   if (t->stride[ndim - 1] != 1) return fail(SWA_ERR_LAYOUT, "%s: innermost stride must be 1", name);
-  if ((reinterpret_cast<uintptr_t>(t->data) & 15) != 0)
-    return fail(SWA_ERR_LAYOUT, "%s: data pointer must be 16-byte aligned", name);
+  if ((reinterpret_cast<uintptr_t>(t->data) % row_align) != 0)
+    return fail(SWA_ERR_LAYOUT, "%s: data pointer must be %d-byte aligned", name, row_align);
   for (int i = 0; i + 1 < ndim; ++i) {
     if (t->stride[i] < 0) return fail(SWA_ERR_LAYOUT, "%s: negative stride in dim %d", name, i);
-    if ((t->stride[i] * es) % 16 != 0)
-      return fail(SWA_ERR_LAYOUT, "%s: stride of dim %d must be a multiple of 16 bytes", name, i);
+    if ((t->stride[i] * es) % row_align != 0)
+      return fail(SWA_ERR_LAYOUT, "%s: stride of dim %d must be a multiple of %d bytes", name, i, row_align);
   }
   return SWA_OK;
 }
@@ -156,7 +156,7 @@ int32_t sparse_mla_fwd(const swa_tensor* q, const swa_tensor* latent, const swa_
   if ((st = check_tensor(q, "q", 3)) != SWA_OK) return st;
   if ((st = check_tensor(latent, "latent", 2)) != SWA_OK) return st;
   if ((st = check_tensor(k_pe, "k_pe", 2)) != SWA_OK) return st;
-  if ((st = check_tensor(indices, "indices", 2)) != SWA_OK) return st;
+  if ((st = check_tensor(indices, "indices", 2, 4)) != SWA_OK) return st;
   if ((st = check_tensor(out, "out", 3)) != SWA_OK) return st;
   if (q->dtype != SWA_DTYPE_BF16 || latent->dtype != SWA_DTYPE_BF16 || k_pe->dtype != SWA_DTYPE_BF16 ||
       out->dtype != SWA_DTYPE_BF16)

@@ -1,6 +1,348 @@
+// Sparse MLA forward for gfx950: each query token attends to the key rows its top-k index
+// row names; a key is latent[idx] (512) + k_pe[idx] (64) and the value is latent[idx].
+// Operation: sparse_mla / MistralLarge4Attention._sparse_forward on the
+// nemo_automodel.components.models.mistral_large4.attention page (-1 = empty slot,
+// empty query rows are zero).
+//
+// Design (one workgroup = 8 waves = one query token x 128 heads):
+//  * Waves w and w+4 (same SIMD) own the same 32 heads (the N dimension of
+//    v_mfma_f32_32x32x16_bf16).  Wave w contracts q.k over the even 16-coordinate
+//    k-steps, wave w+4 over the odd ones; the two partial score tiles are swapped through LDS and summed
+//    (a + b is commutative, so both waves hold bit-identical scores).  Each wave then
+//    accumulates half of the 512 output coordinates.  Per wave: 72 Q registers and 128
+//    fp32 accumulators, two waves per SIMD, equal MFMA work on every SIMD.
+//  * The index row is first compacted in LDS to the slots that are valid (in range,
+//    causal, same document), so invalid slots cost neither gather bytes nor MFMA work.
+//  * Chunks of 32 compacted slots are gathered straight into LDS with
+//    global_load_lds_dwordx4 (no register staging): 32 rows x 72 16-byte units
+//    (64 latent + 8 rotary), unit index swizzled by ^ (row & 7) so the row reads of the
+//    QK^T operand and the ds_read_b64_tr_b16 reads of the PV operand avoid bank
+//    conflicts.  Three buffers: the gather of chunk c+2 is issued right after the score
+//    exchange of chunk c, and the loop is unrolled by three so every LDS read names its
+//    buffer statically (no conservative wait on the gathers in flight).
+//  * S^T = KV Q^T (slots = M, heads = N); online softmax with lazy rescaling (the
+//    reference maximum moves only when a score exceeds it by more than 2^8, which keeps
+//    probabilities <= 256 and the result exact); O^T += latent^T P^T.
 #include "device_common.h"
 #include "launch.h"
 
+#ifndef SWA_SPARSE_QGROUP
+#define SWA_SPARSE_QGROUP 6
+#endif
+#ifndef SWA_SPARSE_PVGROUP
+#define SWA_SPARSE_PVGROUP 2
+#endif
+
 namespace swa {
-hipError_t sparse_mla_fwd_launch(const SparseMlaParams&, hipStream_t) { return hipErrorNotSupported; }
+namespace {
+
+constexpr int kThreads = 512;
+constexpr int kWaves = 8;
+constexpr int kHeadsPerBlock = 128;
+constexpr int kSlots = 32;                          // slots per chunk
+constexpr int kRowUnits = 72;                       // 16-byte units per gathered row
+constexpr int kLatUnits = 64;                       // of which latent
+constexpr int kChunkUnits = kSlots * kRowUnits;     // 2304 = 36 blocks of 64 units
+constexpr int kChunkBlocks = kChunkUnits / 64;      // 36
+constexpr int kSeg = 2048;                          // index slots compacted at a time
+constexpr int kSlotsPerThread = kSeg / kThreads;    // 4
+constexpr int kQFrags = 18;                         // k-steps of 16 coordinates per wave
+constexpr int kDBlocks = 8;                         // 256 output coordinates per wave / 32
+constexpr float kRescaleLog2 = 8.f;                 // lazy-rescale threshold (log2 units)
+constexpr int kQGroup = SWA_SPARSE_QGROUP;          // k-steps between scheduling fences
+constexpr int kPvGroup = SWA_SPARSE_PVGROUP;        // output blocks between scheduling fences
+static_assert(kChunkUnits % 64 == 0, "gather blocks");
+static_assert(kChunkBlocks > 4 * kWaves && kChunkBlocks <= 5 * kWaves, "each wave issues 4 or 5 gathers per chunk");
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) const void glob_cvoid;
+
+// s_waitcnt vmcnt(N) with expcnt / lgkmcnt unconstrained
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// s_waitcnt lgkmcnt(0) with vmcnt / expcnt unconstrained
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
+// workgroup barrier that does not drain outstanding vector-memory loads
+__device__ __forceinline__ void barrier_keep_loads() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+struct Lane {
+  int wave, lane, n, h2, j16, dh, half, hg;
+};
+
+__device__ __forceinline__ void gather_chunk(const SparseMlaParams& p, const int32_t* s_idx, int nv, int chunk,
+                                             int t, u32x4* buf, const Lane& L) {
+  const __bf16* lat = (const __bf16*)p.latent;
+  const __bf16* kpe = (const __bf16*)p.k_pe;
+  // recompute the per-lane gather plan here instead of keeping it live across the loop
+  int lane = L.lane;
+  asm volatile("" : "+v"(lane));
+#pragma unroll
+  for (int i = 0; i < (kChunkBlocks + kWaves - 1) / kWaves; ++i) {
+    const int blk = i * kWaves + L.wave;  // wave-uniform 64-unit block
+    if (blk < kChunkBlocks) {
+      const int u = blk * 64 + lane;
+      const int r = u / kRowUnits;
+      const int qu = u - r * kRowUnits;
+      const int piece = qu ^ (r & 7);
+      const int slot = chunk * kSlots + r;
+      const int idx = slot < nv ? s_idx[slot] : t;  // tail slots read the token's own row (masked)
+      const __bf16* src = piece < kLatUnits ? lat + (int64_t)idx * p.lat_st + piece * 8
+                                            : kpe + (int64_t)idx * p.kpe_st + (piece - kLatUnits) * 8;
+      u32x4* dst = buf + __builtin_amdgcn_readfirstlane(blk * 64);
+      __builtin_amdgcn_global_load_lds((glob_cvoid*)src, (lds_void*)dst, 16, 0, 0);
+    }
+  }
+}
+
+struct SoftmaxState {
+  float mref;  // reference max in log2 units (-inf before the first valid score)
+  float l;     // this half-wave's sum of exp2(score - mref)
+};
+
+// Lane constants are rederived per chunk from an opaque lane id so that none of them stays
+// live (or spilled) across the chunk loop.
+__device__ __forceinline__ Lane opaque_lane(const Lane& Lw) {
+  int lane_op = Lw.lane;
+  asm volatile("" : "+v"(lane_op));
+  Lane L = Lw;
+  L.lane = lane_op;
+  L.n = lane_op & 31;
+  L.h2 = lane_op >> 5;
+  L.j16 = lane_op & 15;
+  L.dh = (lane_op >> 4) & 1;
+  return L;
+}
+
+// Partial S^T[slot][head] over this wave's 18 k-steps of 16 coordinates: global k-step
+// 2 * s + half, i.e. 16-byte units 4 * s + 2 * half + h2 of each gathered row.
+__device__ __forceinline__ f32x16 qk_partial(const u32x4* buf, const bf16x8* qf, const Lane& Lw) {
+  const Lane L = opaque_lane(Lw);
+  f32x16 sc = f32x16{};
+  const int x = L.n & 7;
+  int off[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) off[e] = (4 * e + 2 * L.half + L.h2) ^ x;
+  const u32x4* row = buf + L.n * kRowUnits;
+#pragma unroll
+  for (int s = 0; s < kQFrags; ++s) {
+    const u32x4 a = row[8 * (s >> 1) + off[s & 1]];
+    sc = mfma_bf16_32x32x16(__builtin_bit_cast(bf16x8, a), qf[s], sc);
+  }
+  return sc;
+}
+
+// Online softmax over the chunk's full scores, then O^T[d][head] += latent^T[d][slot] P^T[slot][head]
+// over this wave's 256 output coordinates.
+__device__ __forceinline__ void finish_chunk(const u32x4* buf, f32x16 sc, int n_in_chunk, f32x16* o,
+                                             SoftmaxState& st, float c2, const Lane& Lw) {
+  const Lane L = opaque_lane(Lw);
+  // scores in log2 units; slots past the compacted count are masked
+  if (n_in_chunk < kSlots) {
+#pragma unroll
+    for (int a = 0; a < 16; ++a) {
+      const int r = 8 * (a >> 2) + 4 * L.h2 + (a & 3);
+      sc[a] = r < n_in_chunk ? sc[a] * c2 : -INFINITY;
+    }
+  } else {
+#pragma unroll
+    for (int a = 0; a < 16; ++a) sc[a] *= c2;
+  }
+  float mx = sc[0];
+#pragma unroll
+  for (int a = 1; a < 16; ++a) mx = fmaxf(mx, sc[a]);
+  mx = half_swap_max(mx);
+  // lazy rescale: move the reference only when a score exceeds it by > 2^8 (exact either way)
+  const bool move = mx > st.mref + kRescaleLog2;
+  if (__builtin_amdgcn_ballot_w64(move) != 0) {
+    const float mnew = move ? mx : st.mref;
+    const float alpha = fast_exp2(st.mref - mnew);  // 0 when mref was -inf, 1 when unchanged
+    st.l *= alpha;
+#pragma unroll
+    for (int d = 0; d < kDBlocks; ++d) o[d] *= alpha;
+    st.mref = mnew;
+  }
+  const float mu = st.mref == -INFINITY ? 0.f : st.mref;
+  float rs = 0.f;
+#pragma unroll
+  for (int a = 0; a < 16; ++a) {
+    const float e = fast_exp2(sc[a] - mu);
+    sc[a] = e;
+    rs += e;
+  }
+  st.l += rs;
+  const int r0 = 4 * L.h2 + (L.j16 >> 2);  // + 16 * s for the first read, + 8 for the second
+  const int y = r0 & 7;                     // equal for rows r0 + 16s and r0 + 16s + 8
+  const int xsub = (L.j16 & 3) >> 1;
+  const int half_el = (L.j16 & 1) * 4;      // element offset inside the 16-byte unit
+  int lowp[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) lowp[e] = (4 * e + 2 * L.dh + xsub) ^ y;
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    f32x8 pf;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pf[e] = sc[8 * s + e];
+    const bf16x8 pb = cvt_bf16x8(pf);
+    const __bf16* base0 = (const __bf16*)(buf + (r0 + 16 * s) * kRowUnits + 32 * L.half) + half_el;
+    const __bf16* base1 = base0 + 8 * kRowUnits * 8;
+#pragma unroll
+    for (int d = 0; d < kDBlocks; ++d) {
+      const int unit = 8 * (d >> 1) + lowp[d & 1];
+      const bf16x4 lo4 = lds_read_tr4(base0 + unit * 8);
+      const bf16x4 hi4 = lds_read_tr4(base1 + unit * 8);
+      o[d] = mfma_bf16_32x32x16(__builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7), pb, o[d]);
+    }
+  }
+}
+
+__global__ __launch_bounds__(kThreads, 1) void sparse_mla_fwd_kernel(SparseMlaParams p) {
+  __shared__ int32_t s_idx[kSeg];
+  __shared__ int32_t s_wtot[kWaves];
+  __shared__ f32x4 exch[kWaves * 4 * 64];
+  __shared__ u32x4 buf0[kChunkUnits];
+  __shared__ u32x4 buf1[kChunkUnits];
+  __shared__ u32x4 buf2[kChunkUnits];
+
+  // tokens dealt to XCDs in contiguous ranges (rows of one document share an L2)
+  const int per_xcd = gridDim.x / 8;
+  const int t = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  if (t >= p.T) return;
+
+  Lane L;
+  L.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  L.lane = threadIdx.x & 63;
+  L.n = L.lane & 31;
+  L.h2 = L.lane >> 5;
+  L.j16 = L.lane & 15;
+  L.dh = (L.lane >> 4) & 1;
+  L.half = L.wave >> 2;
+  L.hg = L.wave & 3;
+  const int head = blockIdx.y * kHeadsPerBlock + L.hg * 32 + L.n;
+  const bool head_ok = head < p.H;
+  const bool group_ok = blockIdx.y * kHeadsPerBlock + L.hg * 32 < p.H;
+
+  bf16x8 qf[kQFrags];
+  {
+    const __bf16* qb = (const __bf16*)p.q + (int64_t)t * p.q_st + (int64_t)(head_ok ? head : p.H - 1) * p.q_sh;
+#pragma unroll
+    for (int s = 0; s < kQFrags; ++s) qf[s] = *(const bf16x8*)(qb + 16 * (2 * s + L.half) + 8 * L.h2);
+  }
+  f32x16 o[kDBlocks];
+#pragma unroll
+  for (int d = 0; d < kDBlocks; ++d) o[d] = f32x16{};
+  SoftmaxState st{-INFINITY, 0.f};
+
+  const int my_doc = p.doc_ids[t];
+  const int32_t* irow = p.indices + (int64_t)t * p.idx_st;
+  for (int seg = 0; seg < p.topk; seg += kSeg) {
+    // ---- compact the valid slots of this segment into s_idx (order preserved)
+    __syncthreads();  // previous segment's readers of s_idx and of the buffers are done
+    const int base = seg + threadIdx.x * kSlotsPerThread;
+    int vals[kSlotsPerThread];
+    uint32_t mask = 0;
+    if (my_doc >= 0) {
+#pragma unroll
+      for (int k = 0; k < kSlotsPerThread; ++k) {
+        const int slot = base + k;
+        int idx = -1;
+        if (slot < p.topk) idx = irow[slot];
+        vals[k] = idx;
+        if (idx >= 0 && idx < p.T && idx <= t && p.doc_ids[idx] == my_doc) mask |= 1u << k;
+      }
+    }
+    const int cnt = __builtin_popcount(mask);
+    int incl = cnt;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int yv = __shfl_up(incl, off);
+      if (L.lane >= off) incl += yv;
+    }
+    if (L.lane == 63) s_wtot[L.wave] = incl;
+    __syncthreads();
+    int woff = 0, nv = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const int v = s_wtot[w];
+      woff += w < L.wave ? v : 0;
+      nv += v;
+    }
+    int pos = woff + incl - cnt;
+#pragma unroll
+    for (int k = 0; k < kSlotsPerThread; ++k)
+      if (mask & (1u << k)) s_idx[pos++] = vals[k];
+    __syncthreads();
+
+    // ---- gather + attend, 32 compacted slots per chunk, ring of three buffers.  Chunk cc is
+    // consumed from buffer cc % 3; the gather of chunk cc + 2 is issued once the partial
+    // scores of chunk cc have been exchanged, so it overlaps the rest of chunk cc and all of
+    // chunk cc + 1.  Each wave waits for its own gathers of chunk cc before the barrier.
+    const int nc = (nv + kSlots - 1) / kSlots;
+    if (nc > 0) gather_chunk(p, s_idx, nv, 0, t, buf0, L);
+    if (nc > 1) gather_chunk(p, s_idx, nv, 1, t, buf1, L);
+    auto phase = [&](int cc, const u32x4* cur, u32x4* ahead) {
+      if (cc + 1 < nc) {
+        if (L.wave < kChunkBlocks - 4 * kWaves) wait_vmcnt<5>(); else wait_vmcnt<4>();
+      } else {
+        wait_vmcnt<0>();
+      }
+      barrier_keep_loads();  // chunk cc landed for every wave; chunk cc - 1 fully consumed
+      f32x16 sc = group_ok ? qk_partial(cur, qf, L) : f32x16{};
+      f32x4* mine = exch + L.wave * (4 * 64) + L.lane;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) mine[j * 64] = f32x4{sc[4 * j], sc[4 * j + 1], sc[4 * j + 2], sc[4 * j + 3]};
+      wait_lgkm0();
+      barrier_keep_loads();
+      const f32x4* theirs = exch + (L.wave ^ 4) * (4 * 64) + L.lane;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 v = theirs[j * 64];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sc[4 * j + e] += v[e];
+      }
+      if (cc + 2 < nc) gather_chunk(p, s_idx, nv, cc + 2, t, ahead, L);
+      if (group_ok) finish_chunk(cur, sc, min(kSlots, nv - cc * kSlots), o, st, p.c2, L);
+    };
+    for (int c = 0; c < nc; c += 3) {
+      phase(c, buf0, buf2);
+      if (c + 1 < nc) phase(c + 1, buf1, buf0);
+      if (c + 2 < nc) phase(c + 2, buf2, buf1);
+    }
+  }
+
+  // ---- epilogue
+  if (!head_ok) return;
+  const float lt = half_swap_sum(st.l);
+  const bool empty = st.mref == -INFINITY;
+  const float inv = empty ? 0.f : 1.f / lt;
+  __bf16* ob = (__bf16*)p.out + (int64_t)t * p.o_st + (int64_t)head * p.o_sh + 256 * L.half;
+#pragma unroll
+  for (int d = 0; d < kDBlocks; ++d)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f32x4 r;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) r[e] = o[d][4 * i + e] * inv;
+      *(bf16x4*)(ob + 32 * d + 8 * i + 4 * L.h2) = cvt_bf16x4(r);
+    }
+  if (p.lse != nullptr && L.h2 == 0 && L.half == 0)
+    p.lse[(int64_t)t * p.H + head] = empty ? -INFINITY : (st.mref + __builtin_amdgcn_logf(lt)) * kLn2;
+}
+
+}  // namespace
+
+hipError_t sparse_mla_fwd_launch(const SparseMlaParams& p, hipStream_t stream) {
+  if (p.T <= 0) return hipSuccess;
+  const unsigned gx = (unsigned)((p.T + 7) / 8 * 8);
+  const unsigned gy = (unsigned)((p.H + kHeadsPerBlock - 1) / kHeadsPerBlock);
+  hipLaunchKernelGGL(sparse_mla_fwd_kernel, dim3(gx, gy), dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
 }  // namespace swa

@@ -1,0 +1,172 @@
+"""GPU parity of sparse_mla_fwd (through the C ABI) against the fp64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import sparse_mla_ref, sparse_mla_ref_rows, varlen_attn_ref
+from sliding_window_gqa_varlen_amd import metrics, sparse_mla_fwd, workloads as W
+from tests.golden_util import load
+from tests.gpu_util import BF16_MAX_ABS, assert_lse_match, dev
+
+pytestmark = pytest.mark.gpu
+
+
+def run_sparse(inp, device="cuda:0", with_lse=True, indices=None, doc_ids=None, scale=None):
+    q = dev(inp["q"], torch.bfloat16, device)
+    lat = dev(inp["latent"], torch.bfloat16, device)
+    kpe = dev(inp["k_pe"], torch.bfloat16, device)
+    idx = torch.from_numpy(np.ascontiguousarray(inp["indices"] if indices is None else indices)).to(device)
+    ids = torch.from_numpy(np.ascontiguousarray(inp["doc_ids"] if doc_ids is None else doc_ids)).to(device)
+    out, lse = sparse_mla_fwd(q, lat, kpe, idx, ids, inp["scale"] if scale is None else scale, return_lse=with_lse)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy().astype(np.float64), (None if lse is None else lse.cpu().numpy().astype(np.float64))
+
+
+def check(out, lse, ref_o, ref_l):
+    assert np.all(np.isfinite(out))
+    err = np.abs(out - ref_o).max()
+    assert err <= BF16_MAX_ABS, f"out max abs error {err:.3e}"
+    if lse is not None:
+        assert_lse_match(lse, ref_l, BF16_MAX_ABS)
+
+
+def oracle(inp, indices=None, doc_ids=None):
+    return sparse_mla_ref(inp["q"], inp["latent"], inp["k_pe"], inp["indices"] if indices is None else indices,
+                          inp["doc_ids"] if doc_ids is None else doc_ids, inp["scale"])
+
+
+def small(T, topk, seed=4, H=128, lengths=None, dist=("uniform", 64, 600)):
+    w = W.SparseWorkload("sparse_small", T=T, H=H, d_latent=512, d_rope=64, topk=topk, scale=1.0 / 24.0,
+                         seed=seed, doc_dist=dist, doc_lengths=None if lengths is None else tuple(lengths))
+    return W.make_sparse(w)
+
+
+def test_hand_case_embedded(gpu):
+    """The hand-derived sparse case (d_latent = d_rope = 1), embedded by zero padding."""
+    for case in load("sparse_hand_cases.json"):
+        T, H = case["T"], case["H"]
+        Hp = 16
+        q = np.zeros((T, Hp, 576), np.float32)
+        lat = np.zeros((T, 512), np.float32)
+        kpe = np.zeros((T, 64), np.float32)
+        qc = np.array(case["q"], np.float32)
+        q[:, :H, 0] = qc[..., 0]
+        q[:, :H, 512] = qc[..., 1]
+        lat[:, 0] = np.array(case["latent"])[:, 0]
+        kpe[:, 0] = np.array(case["k_pe"])[:, 0]
+        inp = dict(q=q, latent=lat, k_pe=kpe, indices=np.array(case["indices"], np.int32),
+                   doc_ids=np.array(case["doc_ids"], np.int32), scale=case["scale"])
+        out, lse = run_sparse(inp)
+        exp_o = case["out_expected"][..., 0]
+        np.testing.assert_allclose(out[:, :H, 0], exp_o, rtol=1e-2, atol=1e-2)
+        assert np.all(out[:, :H, 1:] == 0)
+        exp_l = case["lse_expected"]
+        assert np.array_equal(np.isneginf(lse[:, :H]), np.isneginf(exp_l))
+        fin = np.isfinite(exp_l)
+        np.testing.assert_allclose(lse[:, :H][fin], exp_l[fin], rtol=1e-5, atol=1e-5)
+
+
+@pytest.mark.parametrize("T,topk", [(300, 64), (700, 128), (1200, 256)])
+def test_small_workloads_elementwise(gpu, T, topk):
+    inp = small(T, topk, seed=T)
+    ref_o, ref_l = oracle(inp)
+    out, lse = run_sparse(inp)
+    check(out, lse, ref_o, ref_l)
+
+
+def test_full_size_workload_sampled(gpu):
+    inp = W.make_sparse(W.WORKLOADS[4])
+    out, lse = run_sparse(inp)
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
+    rng = np.random.default_rng(0)
+    T = inp["q"].shape[0]
+    cu = np.concatenate([[0], np.cumsum(inp["lengths"])])
+    toks = list(rng.integers(0, T, 40))
+    for d in range(len(cu) - 1):
+        s, e = int(cu[d]), int(cu[d + 1])
+        toks += [s, s + 1, s + 31, s + 32, s + 2047, s + 2048, e - 1]
+    toks = np.array(sorted(set(t for t in toks if 0 <= t < T)))
+    ref_o, ref_l = sparse_mla_ref_rows(inp["q"], inp["latent"], inp["k_pe"], inp["indices"], inp["doc_ids"],
+                                       inp["scale"], toks)
+    check(out[toks], lse[toks], ref_o, ref_l)
+
+
+def test_all_causal_keys_match_dense_attention(gpu):
+    """Selecting every causal same-document key reproduces dense causal MQA (d_qk 576, d_v 512)."""
+    lengths = [100, 37, 200]
+    inp = small(337, 256, seed=11, lengths=lengths)
+    k = np.concatenate([inp["latent"], inp["k_pe"]], axis=1)[:, None, :]
+    v = np.concatenate([inp["latent"], np.zeros_like(inp["k_pe"])], axis=1)[:, None, :]
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    ref_o, ref_l = varlen_attn_ref(inp["q"], k, v, cu, 0, inp["scale"])
+    out, lse = run_sparse(inp)
+    check(out, lse, ref_o[..., :512], ref_l)
+
+
+def test_slot_order_padding_duplicates_and_violations(gpu):
+    inp = small(500, 96, seed=12)
+    base_o, base_l = run_sparse(inp)
+    rng = np.random.default_rng(1)
+    idx = inp["indices"]
+    perm = np.stack([rng.permutation(idx.shape[1]) for _ in range(idx.shape[0])])
+    shuffled = np.take_along_axis(idx, perm, axis=1)
+    o1, l1 = run_sparse(inp, indices=shuffled)
+    assert np.abs(o1 - base_o).max() <= BF16_MAX_ABS and np.abs(l1 - base_l)[np.isfinite(base_l)].max() <= 1e-4
+    # contract violations (future keys, other documents, out of range) act like -1
+    bad = idx.copy()
+    T = bad.shape[0]
+    for t in range(T):
+        free = np.where(bad[t] < 0)[0]
+        junk = [min(t + 1 + k, T + 5) for k in range(3)] + [T, -7, 10 ** 6]
+        for f, j in zip(free, junk):
+            bad[t, f] = j
+    o2, l2 = run_sparse(inp, indices=bad)
+    ref_o, ref_l = oracle(inp, indices=bad)
+    check(o2, l2, ref_o, ref_l)
+    # duplicated slots count once per slot
+    dup = idx.copy()
+    dup[:, -8:] = dup[:, :8]
+    o3, l3 = run_sparse(inp, indices=dup)
+    ref_o, ref_l = oracle(inp, indices=dup)
+    check(o3, l3, ref_o, ref_l)
+
+
+def test_empty_rows_and_padding_tokens(gpu):
+    inp = small(200, 64, seed=13)
+    idx = inp["indices"].copy()
+    idx[50:60] = -1
+    ids = inp["doc_ids"].copy()
+    ids[190:] = -1
+    out, lse = run_sparse(inp, indices=idx, doc_ids=ids)
+    ref_o, ref_l = oracle(inp, indices=idx, doc_ids=ids)
+    check(out, lse, ref_o, ref_l)
+    assert np.all(out[50:60] == 0) and np.all(np.isneginf(lse[50:60]))
+    assert np.all(out[190:] == 0) and np.all(np.isneginf(lse[190:]))
+
+
+@pytest.mark.parametrize("H", [16, 48, 256])
+def test_other_head_counts(gpu, H):
+    inp = small(260, 80, seed=H, H=H)
+    ref_o, ref_l = oracle(inp)
+    out, lse = run_sparse(inp)
+    check(out, lse, ref_o, ref_l)
+
+
+def test_long_index_rows_span_segments(gpu):
+    """topk above the 2048-slot compaction segment, with valid slots in every segment."""
+    lengths = [3000, 1100]
+    inp = small(4100, 2600, seed=14, lengths=lengths)
+    toks = np.array([0, 5, 2047, 2048, 2599, 2600, 2999, 3000, 4099])
+    out, lse = run_sparse(inp)
+    ref_o, ref_l = sparse_mla_ref_rows(inp["q"], inp["latent"], inp["k_pe"], inp["indices"], inp["doc_ids"],
+                                       inp["scale"], toks)
+    check(out[toks], lse[toks], ref_o, ref_l)
+    assert metrics.sparse_valid_slots(inp["indices"], inp["doc_ids"]) > 0
+
+
+def test_repeat_runs_are_bitwise_identical(gpu):
+    inp = small(400, 128, seed=15)
+    o0, l0 = run_sparse(inp)
+    o1, l1 = run_sparse(inp)
+    np.testing.assert_array_equal(o0, o1)
+    np.testing.assert_array_equal(l0, l1)
