@@ -108,6 +108,9 @@ int32_t varlen_attn_fwd(const swa_tensor* q, const swa_tensor* k, const swa_tens
                                  (long long)Hq, (long long)Hkv);
   if (T > (int64_t)1 << 30 || Hq > 65536) return fail(SWA_ERR_UNSUPPORTED, "T or Hq too large");
   if (D != 64 && D != 128) return fail(SWA_ERR_UNSUPPORTED, "head_dim %lld not supported (64 or 128)", (long long)D);
+  // per-tile row offsets are computed in 32 bits: 64 rows x token stride must fit
+  if (k->stride[0] >= (int64_t)1 << 24 || v->stride[0] >= (int64_t)1 << 24)
+    return fail(SWA_ERR_UNSUPPORTED, "k/v token stride must be below 2^24 elements");
   if (n_docs < 0) return fail(SWA_ERR_ARG, "n_docs must be >= 0");
   if (window < 0) return fail(SWA_ERR_ARG, "window must be >= 0");
   if (!std::isfinite(scale) || !(scale > 0.f)) return fail(SWA_ERR_ARG, "scale must be finite and > 0");

@@ -26,6 +26,9 @@
 //    (heaviest first for causal masks).
 //  * Double-buffered K/V tiles: the next tile's global loads are issued before the
 //    current tile's math and written to the other LDS buffer after it.
+//  * Online softmax with lazy rescaling: the reference maximum moves only when a score
+//    exceeds it by more than 2^8 (probabilities stay <= 256), so most tiles skip the O
+//    rescale; the final normalisation uses the same reference, so the result is exact.
 //  * fp32 inputs use v_mfma_f32_32x32x2_f32 with the same accumulator layout.
 #include <type_traits>
 
@@ -38,12 +41,15 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kBN = 64;    // keys per tile
 constexpr int kXcds = 8;   // MI355X: workgroups are dealt round-robin to 8 XCDs
+constexpr float kRescaleLog2 = 8.f;  // lazy-rescale threshold (log2 units)
 
 template <typename T, int D>
 struct Geo {
   static constexpr bool kBf16 = std::is_same<T, __bf16>::value;
   static constexpr int kKPitch = kBf16 ? D + 8 : D + 1;  // LDS row pitch of K (elements)
-  static constexpr int kVPitch = kBf16 ? D + 8 : D;      // LDS row pitch of V
+  // LDS row pitch of V: the transposed reads of one half-wave touch 4 consecutive rows x
+  // 64 bytes, conflict-free on the 64 4-byte banks when the pitch is 16 (mod 64) words
+  static constexpr int kVPitch = kBf16 ? D + 32 : D;
   static constexpr int kKElems = kBN * kKPitch;
   static constexpr int kVElems = kBN * kVPitch;
   static constexpr int kStage = kKElems + kVElems;
@@ -147,24 +153,23 @@ __global__ __launch_bounds__(kThreads, 2) void dense_fwd_kernel(DenseFwdParams p
     }
   }
 
-  // ---- K/V staging through registers
+  // ---- K/V staging through registers.  Rows past the tile's last query are clamped to the
+  // last valid row (always in bounds); every such key lies after every valid query of the
+  // tile, so it is masked to -inf and contributes exactly zero.
   const T* kbase = (const T*)p.k + (int64_t)g * p.k_sh;
   const T* vbase = (const T*)p.v + (int64_t)g * p.v_sh;
   u32x4 kreg[G::kLoads], vreg[G::kLoads];
   auto stage_load = [&](int kb) {
+    const T* kt = kbase + (int64_t)kb * p.k_st;  // wave-uniform tile bases
+    const T* vt = vbase + (int64_t)kb * p.v_st;
+    const int lim = k_hi - 1 - kb;
 #pragma unroll
     for (int i = 0; i < G::kLoads; ++i) {
       const int c = threadIdx.x + i * kThreads;
-      const int row = c / G::kChunksPerRow;
+      const int row = min(c / G::kChunksPerRow, lim);
       const int col = (c % G::kChunksPerRow) * G::kChunk;
-      const int key = kb + row;
-      if (key < k_hi) {
-        kreg[i] = *(const u32x4*)(kbase + (int64_t)key * p.k_st + col);
-        vreg[i] = *(const u32x4*)(vbase + (int64_t)key * p.v_st + col);
-      } else {
-        kreg[i] = u32x4{0, 0, 0, 0};
-        vreg[i] = u32x4{0, 0, 0, 0};
-      }
+      kreg[i] = *(const u32x4*)(kt + (int)(row * p.k_st) + col);
+      vreg[i] = *(const u32x4*)(vt + (int)(row * p.v_st) + col);
     }
   };
   auto stage_store = [&](int buf) {
@@ -191,8 +196,8 @@ __global__ __launch_bounds__(kThreads, 2) void dense_fwd_kernel(DenseFwdParams p
   f32x16 o[G::kDBlocks];
 #pragma unroll
   for (int d = 0; d < G::kDBlocks; ++d) o[d] = f32x16{};
-  float m = -INFINITY;  // running max of raw scores q.k (this lane's column)
-  float l = 0.f;        // running sum of exp2((s - m) * c2) over this half-wave's keys
+  float mref = -INFINITY;  // reference max of the scores in log2 units (scale folded in)
+  float l = 0.f;           // running sum of exp2(s * c2 - mref) over this half-wave's keys
   const float c2 = p.c2;
 
   if (n_tiles > 0) {
@@ -242,24 +247,30 @@ __global__ __launch_bounds__(kThreads, 2) void dense_fwd_kernel(DenseFwdParams p
       for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
         for (int a = 0; a < 16; ++a) mx = fmaxf(mx, sc[blk][a]);
-      mx = half_swap_max(mx);
-      const float m_new = fmaxf(m, mx);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = fast_exp2((m - m_use) * c2);
-      const float mc = m_use * c2;
+      mx = half_swap_max(mx) * c2;
+      // lazy rescale: the reference moves only when a score exceeds it by more than 2^8, so
+      // probabilities stay <= 256 and most tiles skip rescaling O (exact either way)
+      const bool move = mx > mref + kRescaleLog2;
+      if (__builtin_amdgcn_ballot_w64(move) != 0) {
+        const float mnew = move ? mx : mref;
+        // lanes that keep their reference scale by exactly 1 (also when it is still -inf)
+        const float alpha = move ? fast_exp2(mref - mnew) : 1.f;
+        l *= alpha;
+#pragma unroll
+        for (int d = 0; d < G::kDBlocks; ++d) o[d] *= alpha;
+        mref = mnew;
+      }
+      const float mu = mref == -INFINITY ? 0.f : mref;
       float rs = 0.f;
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
         for (int a = 0; a < 16; ++a) {
-          const float e = fast_exp2(__builtin_fmaf(sc[blk][a], c2, -mc));
+          const float e = fast_exp2(__builtin_fmaf(sc[blk][a], c2, -mu));
           sc[blk][a] = e;
           rs += e;
         }
-      l = l * alpha + rs;
-      m = m_new;
-#pragma unroll
-      for (int d = 0; d < G::kDBlocks; ++d) o[d] *= alpha;
+      l += rs;
 
       // O^T += V^T P^T
       if constexpr (G::kBf16) {
@@ -302,7 +313,7 @@ __global__ __launch_bounds__(kThreads, 2) void dense_fwd_kernel(DenseFwdParams p
 
   // ---- epilogue: combine half-wave sums, fold in the sink, normalise once, store
   const float lt = half_swap_sum(l);
-  const float m2 = m * c2;  // running max in log2 units (-inf if nothing was visible)
+  const float m2 = mref;  // reference max in log2 units (-inf if nothing was visible)
   float inv, lse_v;
   if (p.sinks != nullptr) {
     const float s2 = p.sinks[hq] * kLog2e;

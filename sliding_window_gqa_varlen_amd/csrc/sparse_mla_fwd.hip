@@ -15,9 +15,8 @@
 //    causal, same document), so invalid slots cost neither gather bytes nor MFMA work.
 //  * Chunks of 32 compacted slots are gathered straight into LDS with
 //    global_load_lds_dwordx4 (no register staging): 32 rows x 72 16-byte units
-//    (64 latent + 8 rotary), unit index swizzled by ^ (row & 7) so the row reads of the
-//    QK^T operand and the ds_read_b64_tr_b16 reads of the PV operand avoid bank
-//    conflicts.  Three buffers: the gather of chunk c+2 is issued right after the score
+//    (64 latent + 8 rotary), unit index swizzled per row so the row reads of the QK^T
+//    operand and the ds_read_b64_tr_b16 reads of the PV operand avoid bank conflicts.  Three buffers: the gather of chunk c+2 is issued right after the score
 //    exchange of chunk c, and the loop is unrolled by three so every LDS read names its
 //    buffer statically (no conservative wait on the gathers in flight).
 //  * S^T = KV Q^T (slots = M, heads = N); online softmax with lazy rescaling (the
@@ -40,10 +39,13 @@ constexpr int kThreads = 512;
 constexpr int kWaves = 8;
 constexpr int kHeadsPerBlock = 128;
 constexpr int kSlots = 32;                          // slots per chunk
-constexpr int kRowUnits = 72;                       // 16-byte units per gathered row
-constexpr int kLatUnits = 64;                       // of which latent
-constexpr int kChunkUnits = kSlots * kRowUnits;     // 2304 = 36 blocks of 64 units
-constexpr int kChunkBlocks = kChunkUnits / 64;      // 36
+constexpr int kLatUnits = 64;                       // 16-byte latent units per row
+constexpr int kRopeUnits = 8;                       // 16-byte rotary units per row
+constexpr int kLatRegion = kSlots * kLatUnits;      // 2048 units: latent rows
+constexpr int kChunkUnits = kLatRegion + kSlots * kRopeUnits;  // + 256 units: rotary rows
+constexpr int kLatDma = kLatRegion / 64 / kWaves;   // 4 x 16-byte gathers per lane
+constexpr int kRopeDma = kSlots * kRopeUnits * 4 / 64 / kWaves;  // 2 x 4-byte gathers per lane
+constexpr int kDmaPerWave = kLatDma + kRopeDma;     // 6, identical on every wave
 constexpr int kSeg = 2048;                          // index slots compacted at a time
 constexpr int kSlotsPerThread = kSeg / kThreads;    // 4
 constexpr int kQFrags = 18;                         // k-steps of 16 coordinates per wave
@@ -51,8 +53,16 @@ constexpr int kDBlocks = 8;                         // 256 output coordinates pe
 constexpr float kRescaleLog2 = 8.f;                 // lazy-rescale threshold (log2 units)
 constexpr int kQGroup = SWA_SPARSE_QGROUP;          // k-steps between scheduling fences
 constexpr int kPvGroup = SWA_SPARSE_PVGROUP;        // output blocks between scheduling fences
-static_assert(kChunkUnits % 64 == 0, "gather blocks");
-static_assert(kChunkBlocks > 4 * kWaves && kChunkBlocks <= 5 * kWaves, "each wave issues 4 or 5 gathers per chunk");
+static_assert(kLatRegion % (64 * kWaves) == 0 && (kSlots * kRopeUnits * 4) % (64 * kWaves) == 0,
+              "every wave issues the same number of gathers");
+
+// LDS swizzles (64 banks of 4 bytes; 16 lanes x 16 bytes per cycle).  Latent rows are 64
+// 16-byte units; a row read of the QK operand touches one unit of 16 consecutive rows and a
+// transposed read of the PV operand touches 4 consecutive units of 4 consecutive rows.  XOR-ing
+// the low 4 unit bits with rot(r) = ((r & 3) << 2) | ((r >> 2) & 3) spreads both over all 16
+// unit slots.  Rotary rows are 8 units; XOR with (r >> 1) & 7 spreads 16 rows of one unit.
+__device__ __forceinline__ int lat_key(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+__device__ __forceinline__ int rope_key(int r) { return (r >> 1) & 7; }
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) const void glob_cvoid;
@@ -76,6 +86,10 @@ struct Lane {
   int wave, lane, n, h2, j16, dh, half, hg;
 };
 
+// Gather chunk `chunk` (32 compacted slots) into `buf`: latent unit u of row r at
+// r * 64 + (u & 48) + ((u & 15) ^ lat_key(r)), rotary unit u of row r (as four 4-byte pieces)
+// at 2048 + r * 8 + (u ^ rope_key(r)).
+// Slots past the compacted count (and whole chunks past the end) read the token's own row.
 __device__ __forceinline__ void gather_chunk(const SparseMlaParams& p, const int32_t* s_idx, int nv, int chunk,
                                              int t, u32x4* buf, const Lane& L) {
   const __bf16* lat = (const __bf16*)p.latent;
@@ -84,20 +98,28 @@ __device__ __forceinline__ void gather_chunk(const SparseMlaParams& p, const int
   int lane = L.lane;
   asm volatile("" : "+v"(lane));
 #pragma unroll
-  for (int i = 0; i < (kChunkBlocks + kWaves - 1) / kWaves; ++i) {
+  for (int i = 0; i < kLatDma; ++i) {
     const int blk = i * kWaves + L.wave;  // wave-uniform 64-unit block
-    if (blk < kChunkBlocks) {
-      const int u = blk * 64 + lane;
-      const int r = u / kRowUnits;
-      const int qu = u - r * kRowUnits;
-      const int piece = qu ^ (r & 7);
-      const int slot = chunk * kSlots + r;
-      const int idx = slot < nv ? s_idx[slot] : t;  // tail slots read the token's own row (masked)
-      const __bf16* src = piece < kLatUnits ? lat + (int64_t)idx * p.lat_st + piece * 8
-                                            : kpe + (int64_t)idx * p.kpe_st + (piece - kLatUnits) * 8;
-      u32x4* dst = buf + __builtin_amdgcn_readfirstlane(blk * 64);
-      __builtin_amdgcn_global_load_lds((glob_cvoid*)src, (lds_void*)dst, 16, 0, 0);
-    }
+    const int u = blk * 64 + lane;
+    const int r = u >> 6;
+    const int piece = (u & 48) | ((u & 15) ^ lat_key(r));
+    const int slot = chunk * kSlots + r;
+    const int idx = slot < nv ? s_idx[slot] : t;
+    u32x4* dst = buf + __builtin_amdgcn_readfirstlane(blk * 64);
+    __builtin_amdgcn_global_load_lds((glob_cvoid*)(lat + (int64_t)idx * p.lat_st + piece * 8), (lds_void*)dst,
+                                     16, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < kRopeDma; ++i) {
+    const int blk = i * kWaves + L.wave;  // wave-uniform 64-dword block of the rotary region
+    const int dw = blk * 64 + lane;       // dword index in the rotary region
+    const int r = dw >> 5;
+    const int unit = ((dw >> 2) & 7) ^ rope_key(r);
+    const int slot = chunk * kSlots + r;
+    const int idx = slot < nv ? s_idx[slot] : t;
+    uint32_t* dst = (uint32_t*)(buf + kLatRegion) + __builtin_amdgcn_readfirstlane(blk * 64);
+    __builtin_amdgcn_global_load_lds((glob_cvoid*)(kpe + (int64_t)idx * p.kpe_st + unit * 8 + (dw & 3) * 2),
+                                     (lds_void*)dst, 4, 0, 0);
   }
 }
 
@@ -125,14 +147,19 @@ __device__ __forceinline__ Lane opaque_lane(const Lane& Lw) {
 __device__ __forceinline__ f32x16 qk_partial(const u32x4* buf, const bf16x8* qf, const Lane& Lw) {
   const Lane L = opaque_lane(Lw);
   f32x16 sc = f32x16{};
-  const int x = L.n & 7;
-  int off[2];
+  const int lk = lat_key(L.n);
+  const int rk = rope_key(L.n);
+  int off[4];
 #pragma unroll
-  for (int e = 0; e < 2; ++e) off[e] = (4 * e + 2 * L.half + L.h2) ^ x;
-  const u32x4* row = buf + L.n * kRowUnits;
+  for (int j = 0; j < 4; ++j) off[j] = (4 * j + 2 * L.half + L.h2) ^ lk;
+  const int lat_row = L.n * kLatUnits;
+  const int rope_row = kLatRegion + L.n * kRopeUnits;
 #pragma unroll
   for (int s = 0; s < kQFrags; ++s) {
-    const u32x4 a = row[8 * (s >> 1) + off[s & 1]];
+    // k-step s covers latent units 4s + 2 half + h2 (s < 16), then rotary units 4(s-16) + 2 half + h2
+    const int unit = s < 16 ? lat_row + 16 * (s >> 2) + off[s & 3]
+                            : rope_row + ((4 * (s - 16) + 2 * L.half + L.h2) ^ rk);
+    const u32x4 a = buf[unit];
     sc = mfma_bf16_32x32x16(__builtin_bit_cast(bf16x8, a), qf[s], sc);
   }
   return sc;
@@ -162,7 +189,8 @@ __device__ __forceinline__ void finish_chunk(const u32x4* buf, f32x16 sc, int n_
   const bool move = mx > st.mref + kRescaleLog2;
   if (__builtin_amdgcn_ballot_w64(move) != 0) {
     const float mnew = move ? mx : st.mref;
-    const float alpha = fast_exp2(st.mref - mnew);  // 0 when mref was -inf, 1 when unchanged
+    // lanes that keep their reference scale by exactly 1 (also when it is still -inf)
+    const float alpha = move ? fast_exp2(st.mref - mnew) : 1.f;
     st.l *= alpha;
 #pragma unroll
     for (int d = 0; d < kDBlocks; ++d) o[d] *= alpha;
@@ -177,26 +205,34 @@ __device__ __forceinline__ void finish_chunk(const u32x4* buf, f32x16 sc, int n_
     rs += e;
   }
   st.l += rs;
-  const int r0 = 4 * L.h2 + (L.j16 >> 2);  // + 16 * s for the first read, + 8 for the second
-  const int y = r0 & 7;                     // equal for rows r0 + 16s and r0 + 16s + 8
+  // transposed reads: lane j of a 16-lane group reads row r0 + 16 s (+ 8) and the 8-byte half
+  // (j & 1) of latent unit 32 half + 4 d + 2 dh + ((j & 3) >> 1); rows r0 and r0 + 8 differ
+  // only in bit 3, which flips bit 1 of lat_key
+  const int r0 = 4 * L.h2 + (L.j16 >> 2);
   const int xsub = (L.j16 & 3) >> 1;
   const int half_el = (L.j16 & 1) * 4;      // element offset inside the 16-byte unit
-  int lowp[2];
+  const int key0 = lat_key(r0);
+  int lowp[4];
 #pragma unroll
-  for (int e = 0; e < 2; ++e) lowp[e] = (4 * e + 2 * L.dh + xsub) ^ y;
+  for (int e = 0; e < 4; ++e) lowp[e] = (4 * e + 2 * L.dh + xsub) ^ key0;
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
     f32x8 pf;
 #pragma unroll
     for (int e = 0; e < 8; ++e) pf[e] = sc[8 * s + e];
     const bf16x8 pb = cvt_bf16x8(pf);
-    const __bf16* base0 = (const __bf16*)(buf + (r0 + 16 * s) * kRowUnits + 32 * L.half) + half_el;
-    const __bf16* base1 = base0 + 8 * kRowUnits * 8;
+    const __bf16* elems = (const __bf16*)buf;
+    const int off0 = ((r0 + 16 * s) * kLatUnits + 32 * L.half) * 8 + half_el;
 #pragma unroll
     for (int d = 0; d < kDBlocks; ++d) {
-      const int unit = 8 * (d >> 1) + lowp[d & 1];
-      const bf16x4 lo4 = lds_read_tr4(base0 + unit * 8);
-      const bf16x4 hi4 = lds_read_tr4(base1 + unit * 8);
+      const int unit = 16 * (d >> 2) + lowp[d & 3];
+      // one integer index per read keeps the pointer a single GEP from the LDS buffer, so the
+      // read keeps the buffer's alias scope (no wait on gathers into the other buffers)
+      const int i_lo = off0 + unit * 8;
+      const int i_hi = off0 + 8 * kLatUnits * 8 + (unit ^ 2) * 8;
+      asm volatile("" ::"v"(i_hi));
+      const bf16x4 lo4 = lds_read_tr4(&elems[i_lo]);
+      const bf16x4 hi4 = lds_read_tr4(&elems[i_hi]);
       o[d] = mfma_bf16_32x32x16(__builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7), pb, o[d]);
     }
   }
@@ -280,40 +316,44 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_fwd_kernel(SparseMlaPa
     __syncthreads();
 
     // ---- gather + attend, 32 compacted slots per chunk, ring of three buffers.  Chunk cc is
-    // consumed from buffer cc % 3; the gather of chunk cc + 2 is issued once the partial
-    // scores of chunk cc have been exchanged, so it overlaps the rest of chunk cc and all of
-    // chunk cc + 1.  Each wave waits for its own gathers of chunk cc before the barrier.
+    // consumed from buffer cc % 3; the gather of chunk cc + 2 is issued once the partial scores
+    // of chunk cc have been exchanged, so it overlaps the rest of chunk cc and all of chunk
+    // cc + 1.  Every wave issues exactly kDmaPerWave gathers per chunk (dummy ones past the
+    // end), so "own gathers of chunk cc landed" is vmcnt <= kDmaPerWave.
     const int nc = (nv + kSlots - 1) / kSlots;
-    if (nc > 0) gather_chunk(p, s_idx, nv, 0, t, buf0, L);
-    if (nc > 1) gather_chunk(p, s_idx, nv, 1, t, buf1, L);
-    auto phase = [&](int cc, const u32x4* cur, u32x4* ahead) {
-      if (cc + 1 < nc) {
-        if (L.wave < kChunkBlocks - 4 * kWaves) wait_vmcnt<5>(); else wait_vmcnt<4>();
-      } else {
-        wait_vmcnt<0>();
-      }
+    if (nc > 0) {  // both prologue gathers unconditionally (chunk 1 may be a dummy)
+      gather_chunk(p, s_idx, nv, 0, t, buf0, L);
+      gather_chunk(p, s_idx, nv, 1, t, buf1, L);
+    }
+    auto phase = [&](int cc, const u32x4* cur, u32x4* ahead, bool steady) {
+      if (steady) wait_vmcnt<kDmaPerWave>(); else wait_vmcnt<0>();
       barrier_keep_loads();  // chunk cc landed for every wave; chunk cc - 1 fully consumed
       f32x16 sc = group_ok ? qk_partial(cur, qf, L) : f32x16{};
-      f32x4* mine = exch + L.wave * (4 * 64) + L.lane;
+      const int xl = opaque_lane(L).lane;  // rederived, not kept live across the loop
+      f32x4* mine = exch + L.wave * (4 * 64) + xl;
 #pragma unroll
       for (int j = 0; j < 4; ++j) mine[j * 64] = f32x4{sc[4 * j], sc[4 * j + 1], sc[4 * j + 2], sc[4 * j + 3]};
       wait_lgkm0();
       barrier_keep_loads();
-      const f32x4* theirs = exch + (L.wave ^ 4) * (4 * 64) + L.lane;
+      const f32x4* theirs = exch + (L.wave ^ 4) * (4 * 64) + xl;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const f32x4 v = theirs[j * 64];
 #pragma unroll
         for (int e = 0; e < 4; ++e) sc[4 * j + e] += v[e];
       }
-      if (cc + 2 < nc) gather_chunk(p, s_idx, nv, cc + 2, t, ahead, L);
+      if (steady) gather_chunk(p, s_idx, nv, cc + 2, t, ahead, L);
       if (group_ok) finish_chunk(cur, sc, min(kSlots, nv - cc * kSlots), o, st, p.c2, L);
     };
-    for (int c = 0; c < nc; c += 3) {
-      phase(c, buf0, buf2);
-      if (c + 1 < nc) phase(c + 1, buf1, buf0);
-      if (c + 2 < nc) phase(c + 2, buf2, buf1);
+    int c = 0;
+    for (; c + 2 < nc; c += 3) {  // full rounds: chunks c, c+1, c+2 all exist
+      phase(c, buf0, buf2, true);
+      phase(c + 1, buf1, buf0, true);
+      phase(c + 2, buf2, buf1, true);
     }
+    // the last one or two chunks were gathered by the rounds above (or the prologue)
+    if (c < nc) phase(c, buf0, buf2, false);
+    if (c + 1 < nc) phase(c + 1, buf1, buf0, false);
   }
 
   // ---- epilogue

@@ -116,6 +116,17 @@ def test_windows(gpu, window):
     assert_dense_parity("bf16", out, lse, ref_o, ref_l)
 
 
+@pytest.mark.parametrize("Hq,Hkv", [(4, 4), (5, 1)])
+def test_fully_masked_lanes_beside_visible_ones(gpu, Hq, Hkv):
+    """One query head per fold puts 32 consecutive tokens in a wave; with a short window the
+    first key tile is fully masked for the wave's last tokens while visible to its first ones."""
+    lengths = [40, 200, 300]
+    inp = custom(lengths, T=540, Hq=Hq, Hkv=Hkv, D=128, window=9, dtype="bf16", sinks=False, seed=21)
+    ref_o, ref_l = oracle_full(inp)
+    out, lse = run_dense(inp, "bf16")
+    assert_dense_parity("bf16", out, lse, ref_o, ref_l)
+
+
 def test_window_one_returns_v(gpu):
     inp = custom([70, 3, 90], T=163, Hq=4, Hkv=1, D=128, window=1, dtype="f32", seed=3)
     out, _ = run_dense(inp, "f32")
