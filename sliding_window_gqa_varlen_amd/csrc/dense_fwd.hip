@@ -12,11 +12,11 @@
 //    four waves stack along tokens, so a workgroup owns TQ = 128 / HB tokens x HB heads
 //    and every key/value tile staged in LDS serves all 128 columns (GQA head-group reuse).
 //  * Transposed scores.  S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (keys = M, query
-//    columns = N): each lane ends up holding one query column and 16 keys of every
-//    32-key block, so the softmax row statistics are lane-local except for one
-//    permlane32 swap with the other half-wave, and the probabilities already sit in the
-//    B-operand layout of O^T += V^T P^T.  V stays row-major in LDS; its transposed
-//    A operand comes from ds_read_b64_tr_b16.
+//    columns = N): each lane holds one query column and 16 keys of every 32-key block, so
+//    the softmax row statistics are lane-local except for one permlane32 swap with the
+//    other half-wave, and the probabilities already sit in the B-operand layout of
+//    O^T += V^T P^T.  V stays row-major in LDS; its transposed A operand comes from
+//    ds_read_b64_tr_b16.
 //  * Per-document tiling.  Query tiles start at document starts (virtual tile index
 //    v -> segment by binary search over cu_seqlens, no host round trip), key tiles cover
 //    only [max(doc start, first query - window + 1), last query]; masks are evaluated
@@ -24,12 +24,19 @@
 //  * Scheduling.  Blocks are remapped so that all tiles of one KV head land on the same
 //    XCD (its L2 holds that head's K/V), and each document's tiles run last-first
 //    (heaviest first for causal masks).
-//  * Double-buffered K/V tiles: the next tile's global loads are issued before the
-//    current tile's math and written to the other LDS buffer after it.
+//  * bf16 pipeline.  64-key K and V tiles arrive by global_load_lds_dwordx4 straight into
+//    two LDS buffers each (no register staging); iteration j issues the MFMAs of
+//    S(j) = K(j) Q^T, runs the online softmax of tile j-1 in their shadow, then
+//    O += V(j-1) P(j-1), while K(j+1) and V(j) are in flight.  Buffers are separate
+//    __shared__ arrays named statically (the loop is unrolled by two), so no LDS read
+//    waits on a transfer into another buffer.  Rows are XOR-swizzled for the 64-bank
+//    LDS: K for row reads of 16 rows at one unit, V for transposed reads of 4 rows x 4
+//    units.
 //  * Online softmax with lazy rescaling: the reference maximum moves only when a score
 //    exceeds it by more than 2^8 (probabilities stay <= 256), so most tiles skip the O
 //    rescale; the final normalisation uses the same reference, so the result is exact.
-//  * fp32 inputs use v_mfma_f32_32x32x2_f32 with the same accumulator layout.
+//  * fp32 inputs use v_mfma_f32_32x32x2_f32 with the same accumulator layout and a
+//    register-staged, padded LDS layout (parity path, not tuned).
 #include <type_traits>
 
 #include "device_common.h"
@@ -42,27 +49,26 @@ constexpr int kThreads = 256;
 constexpr int kBN = 64;    // keys per tile
 constexpr int kXcds = 8;   // MI355X: workgroups are dealt round-robin to 8 XCDs
 constexpr float kRescaleLog2 = 8.f;  // lazy-rescale threshold (log2 units)
+#ifndef SWA_KAHEAD128
+#define SWA_KAHEAD128 4
+#endif
 
-template <typename T, int D>
-struct Geo {
-  static constexpr bool kBf16 = std::is_same<T, __bf16>::value;
-  static constexpr int kKPitch = kBf16 ? D + 8 : D + 1;  // LDS row pitch of K (elements)
-  // LDS row pitch of V: the transposed reads of one half-wave touch 4 consecutive rows x
-  // 64 bytes, conflict-free on the 64 4-byte banks when the pitch is 16 (mod 64) words
-  static constexpr int kVPitch = kBf16 ? D + 32 : D;
-  static constexpr int kKElems = kBN * kKPitch;
-  static constexpr int kVElems = kBN * kVPitch;
-  static constexpr int kStage = kKElems + kVElems;
-  static constexpr int kQFrags = kBf16 ? D / 16 : D / 2;
-  static constexpr int kDBlocks = D / 32;
-  static constexpr int kChunk = 16 / (int)sizeof(T);      // elements per 16-byte chunk
-  static constexpr int kChunksPerRow = D / kChunk;
-  static constexpr int kLoads = kBN * kChunksPerRow / kThreads;  // chunks per thread per tensor
-  static_assert(kBN * kChunksPerRow % kThreads == 0, "tile must split evenly over threads");
-};
+typedef __attribute__((address_space(3))) void lds_void;
+constexpr int kBufferWord3 = 0x00020000;  // buffer descriptor word 3: 32-bit data format, raw access
+typedef __attribute__((address_space(1))) const void glob_cvoid;
 
-template <typename T>
-using QFragT = typename std::conditional<std::is_same<T, __bf16>::value, bf16x8, float>::type;
+// s_waitcnt vmcnt(0) with expcnt / lgkmcnt unconstrained
+__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8)); }
+// workgroup barrier that does not drain outstanding vector-memory loads
+__device__ __forceinline__ void barrier_keep_loads() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
 
 // Segment boundaries: segment 0 = [0, cu[0]) and segment n+1 = [cu[n], T) are padding,
 // segment s in 1..n is document s-1.  Entries are clamped to [0, T].
@@ -73,250 +79,182 @@ __device__ __forceinline__ int seg_bound(const DenseFwdParams& p, int s) {
   return x < 0 ? 0 : (x > p.T ? p.T : x);
 }
 
-template <typename T, int D>
-__device__ __forceinline__ void write_padding(const DenseFwdParams& p, int t0, int t_end, int h0, int HB) {
-  // zero rows [t0, t_end) x heads [h0, h0 + HB); lse = -inf
-  T* out = (T*)p.out;
-  constexpr int kC = 16 / (int)sizeof(T);
-  const int per_row = D / kC;
-  const int n_rows = (t_end - t0) * HB;
-  for (int idx = threadIdx.x; idx < n_rows * per_row; idx += kThreads) {
-    const int row = idx / per_row, c = idx - row * per_row;
-    const int t = t0 + row / HB, h = h0 + row % HB;
-    *(u32x4*)(out + (int64_t)t * p.o_st + (int64_t)h * p.o_sh + c * kC) = u32x4{0, 0, 0, 0};
-  }
-  if (p.lse != nullptr)
-    for (int idx = threadIdx.x; idx < n_rows; idx += kThreads)
-      p.lse[(int64_t)(t0 + idx / HB) * p.Hq + h0 + idx % HB] = -INFINITY;
-}
+// The workgroup's query tile: tokens [t0, t_end) of segment `seg`, heads [h0, h0 + HB).
+struct Tile {
+  int g, h0, HB, t0, t_end, seg_start, seg;
+  bool padding;
+};
 
-template <typename T, int D>
-__global__ __launch_bounds__(kThreads, 2) void dense_fwd_kernel(DenseFwdParams p) {
-  using G = Geo<T, D>;
-  __shared__ __attribute__((aligned(16))) T smem[2 * G::kStage];
-
-  // ---- work item: XCD-aware remap, then (KV head, head chunk, virtual tile)
+// Decodes blockIdx into a tile; returns false for idle blocks.
+__device__ __forceinline__ bool decode_tile(const DenseFwdParams& p, Tile& w) {
   const int per_xcd = gridDim.x / kXcds;
-  const int L = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
-  if (L >= p.n_work) return;
+  const int L = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;  // XCD-aware remap
+  if (L >= p.n_work) return false;
   const int VT = p.n_vtiles;
   const int hc = L / VT;
-  const int v = VT - 1 - (L - hc * VT);
-  const int g = hc / p.n_chunks;
-  const int chunk = hc - g * p.n_chunks;
+  const int v = VT - 1 - (L - hc * VT);  // each document's tiles last-first
+  w.g = hc / p.n_chunks;
+  const int chunk = hc - w.g * p.n_chunks;
   const int TQ = p.tile_tokens;
-
   // segment s holding virtual tile v: A(s) = floor(bound(s) / TQ) + s, A(s) <= v < A(s+1)
   int lo = 0, hi = p.n_docs + 2;
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
     if (seg_bound(p, mid) / TQ + mid <= v) lo = mid; else hi = mid;
   }
-  const int seg_start = seg_bound(p, lo);
+  w.seg = lo;
+  w.seg_start = seg_bound(p, lo);
   const int seg_end = seg_bound(p, lo + 1);
-  const int t0 = seg_start + (v - (seg_start / TQ + lo)) * TQ;
-  if (t0 >= seg_end) return;
-  const int t_end = min(t0 + TQ, seg_end);
-  const int HB = 1 << p.hb_shift;
-  const int h0 = g * p.G + chunk * HB;
-  if (lo == 0 || lo == p.n_docs + 1) {
-    write_padding<T, D>(p, t0, t_end, h0, HB);
-    return;
-  }
+  w.t0 = w.seg_start + (v - (w.seg_start / TQ + lo)) * TQ;
+  if (w.t0 >= seg_end) return false;
+  w.t_end = min(w.t0 + TQ, seg_end);
+  w.HB = 1 << p.hb_shift;
+  w.h0 = w.g * p.G + chunk * w.HB;
+  w.padding = (lo == 0 || lo == p.n_docs + 1);
+  return true;
+}
 
-  // ---- lane geometry
-  const int wave = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63;
-  const int n = lane & 31;   // query column of this lane
-  const int h2 = lane >> 5;  // half-wave
+template <typename T, int D>
+__device__ __forceinline__ void write_padding(const DenseFwdParams& p, const Tile& w) {
+  // zero rows [t0, t_end) x heads [h0, h0 + HB); lse = -inf
+  T* out = (T*)p.out;
+  constexpr int kC = 16 / (int)sizeof(T);
+  const int per_row = D / kC;
+  const int n_rows = (w.t_end - w.t0) * w.HB;
+  for (int idx = threadIdx.x; idx < n_rows * per_row; idx += kThreads) {
+    const int row = idx / per_row, c = idx - row * per_row;
+    const int t = w.t0 + row / w.HB, h = w.h0 + row % w.HB;
+    *(u32x4*)(out + (int64_t)t * p.o_st + (int64_t)h * p.o_sh + c * kC) = u32x4{0, 0, 0, 0};
+  }
+  if (p.lse != nullptr)
+    for (int idx = threadIdx.x; idx < n_rows; idx += kThreads)
+      p.lse[(int64_t)(w.t0 + idx / w.HB) * p.Hq + w.h0 + idx % w.HB] = -INFINITY;
+}
+
+// Per-lane query geometry inside the tile.
+struct Cols {
+  int wave, lane, n, h2, tw0, tw1, tq, hq, k_lo, k_hi, n_tiles, W;
+};
+
+__device__ __forceinline__ Cols make_cols(const DenseFwdParams& p, const Tile& w) {
+  Cols c;
+  c.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  c.lane = threadIdx.x & 63;
+  c.n = c.lane & 31;   // query column of this lane
+  c.h2 = c.lane >> 5;  // half-wave
   const int TW = 32 >> p.hb_shift;
-  const int tw0 = t0 + wave * TW;
-  const int tw1 = min(tw0 + TW, t_end) - 1;
-  const int tq = tw0 + (n >> p.hb_shift);
-  const int hq = h0 + (n & (HB - 1));
-  const int W = p.window;
-  const int s_d = seg_start;
-  const int k_lo = W ? max(s_d, t0 - W + 1) : s_d;
-  const int k_hi = t_end;
-  const int n_tiles = (k_hi - k_lo + kBN - 1) / kBN;
+  c.tw0 = w.t0 + c.wave * TW;
+  c.tw1 = min(c.tw0 + TW, w.t_end) - 1;  // last valid token of this wave (< tw0 if none)
+  c.tq = c.tw0 + (c.n >> p.hb_shift);
+  c.hq = w.h0 + (c.n & (w.HB - 1));
+  c.W = p.window;
+  c.k_lo = c.W ? max(w.seg_start, w.t0 - c.W + 1) : w.seg_start;
+  c.k_hi = w.t_end;
+  c.n_tiles = (c.k_hi - c.k_lo + kBN - 1) / kBN;
+  return c;
+}
 
-  // ---- Q fragments (B operand of S^T = K Q^T), kept in registers
-  QFragT<T> qf[G::kQFrags];
-  {
-    const T* qb = (const T*)p.q + (int64_t)min(tq, t_end - 1) * p.q_st + (int64_t)hq * p.q_sh;
-    if constexpr (G::kBf16) {
+// Does the wave see any key of the tile starting at kb?  Does the tile need masking?
+__device__ __forceinline__ bool tile_active(const Cols& c, int kb) {
+  return (c.tw0 <= c.tw1) && (kb <= c.tw1) && (c.W == 0 || kb + kBN - 1 > c.tw0 - c.W);
+}
+__device__ __forceinline__ bool tile_needs_mask(const Cols& c, int kb) {
+  return (kb + kBN - 1 > c.tw0) || (c.W != 0 && kb <= c.tw1 - c.W);
+}
+
+struct Softmax {
+  float mref;  // reference max of the scores in log2 units (scale folded in)
+  float l;     // running sum of exp2(s * c2 - mref) over this half-wave's keys
+};
+
+// Masks keys outside [doc start, query] and outside the window (tiles that straddle the
+// diagonal or the window edge only).
+__device__ __forceinline__ void mask_tile(f32x16 (&sc)[2], int kb, const Cols& c) {
+  // allowed keys of this lane's query: kb + off with lo <= off <= lo + range, where
+  // off = 32 blk + 8 (a / 4) + 4 h2 + a % 4; the 4 h2 term is folded into lo so every
+  // comparison is against an immediate: one subtract, one unsigned compare, one select
+  const int tq4 = opaque(c.tq - 4 * c.h2);  // recomputed per use, nothing hoisted out of the loop
+  const int lo = c.W ? tq4 - c.W + 1 - kb : -(1 << 30);
+  const unsigned range = (unsigned)(tq4 - kb - lo);
 #pragma unroll
-      for (int s = 0; s < G::kQFrags; ++s) qf[s] = *(const bf16x8*)(qb + 16 * s + 8 * h2);
-    } else {
+  for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-      for (int s = 0; s < G::kQFrags; ++s) qf[s] = qb[2 * s + h2];
+    for (int a = 0; a < 16; ++a) {
+      const int off = 32 * blk + 8 * (a >> 2) + (a & 3);
+      sc[blk][a] = (unsigned)(off - lo) <= range ? sc[blk][a] : -INFINITY;
     }
+}
+
+// Online-softmax statistics of one tile, from this lane's raw score maximum.  Lazy
+// rescale: the reference max moves only when a score exceeds it by more than 2^8, so
+// probabilities stay <= 256 and most tiles leave O alone (exact either way); lanes that
+// keep their reference scale by exactly 1, also while it is -inf.  `alpha` is the factor
+// O and l must be scaled by, `mu` the exponent offset of the probabilities (0 while
+// nothing was visible).
+struct TileStats {
+  float alpha, mu;
+  bool move;
+};
+__device__ __forceinline__ TileStats tile_stats(float lane_max, float c2, Softmax& st) {
+  const float mx = half_swap_max(lane_max) * c2;
+  TileStats t;
+  t.move = mx > st.mref + kRescaleLog2;
+  const float mnew = t.move ? mx : st.mref;
+  t.alpha = t.move ? fast_exp2(st.mref - mnew) : 1.f;
+  st.mref = mnew;
+  t.mu = mnew == -INFINITY ? 0.f : mnew;
+  return t;
+}
+__device__ __forceinline__ float lane_max(const f32x16 (&sc)[2]) {
+  float mx = -INFINITY;
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+    for (int a = 0; a < 16; ++a) mx = fmaxf(mx, sc[blk][a]);
+  return mx;
+}
+
+// Scores -> unnormalised probabilities exp2(s * c2 - mu), in place; returns their sum.
+__device__ __forceinline__ float tile_exp(f32x16 (&sc)[2], float c2, float mu) {
+  float rs = 0.f;
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+    for (int a = 0; a < 16; ++a) {
+      const float e = fast_exp2(__builtin_fmaf(sc[blk][a], c2, -mu));
+      sc[blk][a] = e;
+      rs += e;
+    }
+  return rs;
+}
+
+template <int DB>
+__device__ __forceinline__ void rescale_o(bool move, float alpha, f32x16 (&o)[DB]) {
+  if (__builtin_amdgcn_ballot_w64(move) != 0) {
+#pragma unroll
+    for (int d = 0; d < DB; ++d) o[d] *= alpha;
   }
+}
 
-  // ---- K/V staging through registers.  Rows past the tile's last query are clamped to the
-  // last valid row (always in bounds); every such key lies after every valid query of the
-  // tile, so it is masked to -inf and contributes exactly zero.
-  const T* kbase = (const T*)p.k + (int64_t)g * p.k_sh;
-  const T* vbase = (const T*)p.v + (int64_t)g * p.v_sh;
-  u32x4 kreg[G::kLoads], vreg[G::kLoads];
-  auto stage_load = [&](int kb) {
-    const T* kt = kbase + (int64_t)kb * p.k_st;  // wave-uniform tile bases
-    const T* vt = vbase + (int64_t)kb * p.v_st;
-    const int lim = k_hi - 1 - kb;
-#pragma unroll
-    for (int i = 0; i < G::kLoads; ++i) {
-      const int c = threadIdx.x + i * kThreads;
-      const int row = min(c / G::kChunksPerRow, lim);
-      const int col = (c % G::kChunksPerRow) * G::kChunk;
-      kreg[i] = *(const u32x4*)(kt + (int)(row * p.k_st) + col);
-      vreg[i] = *(const u32x4*)(vt + (int)(row * p.v_st) + col);
-    }
-  };
-  auto stage_store = [&](int buf) {
-    T* Ks = smem + buf * G::kStage;
-    T* Vs = Ks + G::kKElems;
-#pragma unroll
-    for (int i = 0; i < G::kLoads; ++i) {
-      const int c = threadIdx.x + i * kThreads;
-      const int row = c / G::kChunksPerRow;
-      const int col = (c % G::kChunksPerRow) * G::kChunk;
-      if constexpr (G::kBf16) {
-        *(u32x4*)(Ks + row * G::kKPitch + col) = kreg[i];
-      } else {
-        float* kd = (float*)(Ks + row * G::kKPitch + col);  // odd pitch: scalar stores
-        kd[0] = __uint_as_float(kreg[i][0]);
-        kd[1] = __uint_as_float(kreg[i][1]);
-        kd[2] = __uint_as_float(kreg[i][2]);
-        kd[3] = __uint_as_float(kreg[i][3]);
-      }
-      *(u32x4*)(Vs + row * G::kVPitch + col) = vreg[i];
-    }
-  };
+// Full online-softmax step for one tile (used where nothing is interleaved with it).
+template <int DB>
+__device__ __forceinline__ void softmax_tile(f32x16 (&sc)[2], bool need_mask, int kb, const Cols& c, float c2,
+                                             Softmax& st, f32x16 (&o)[DB]) {
+  if (need_mask) mask_tile(sc, kb, c);
+  const TileStats t = tile_stats(lane_max(sc), c2, st);
+  rescale_o<DB>(t.move, t.alpha, o);
+  st.l = st.l * t.alpha + tile_exp(sc, c2, t.mu);
+}
 
-  f32x16 o[G::kDBlocks];
-#pragma unroll
-  for (int d = 0; d < G::kDBlocks; ++d) o[d] = f32x16{};
-  float mref = -INFINITY;  // reference max of the scores in log2 units (scale folded in)
-  float l = 0.f;           // running sum of exp2(s * c2 - mref) over this half-wave's keys
-  const float c2 = p.c2;
-
-  if (n_tiles > 0) {
-    stage_load(k_lo);
-    stage_store(0);
-  }
-  __syncthreads();
-
-  for (int j = 0; j < n_tiles; ++j) {
-    const int kb = k_lo + j * kBN;
-    if (j + 1 < n_tiles) stage_load(kb + kBN);
-    const T* Ks = smem + (j & 1) * G::kStage;
-    const T* Vs = Ks + G::kKElems;
-    const bool active = (tw0 <= tw1) && (kb <= tw1) && (W == 0 || kb + kBN - 1 > tw0 - W);
-    if (active) {
-      // S^T for two 32-key blocks
-      f32x16 sc[2];
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk) {
-        sc[blk] = f32x16{};
-        const T* krow = Ks + (32 * blk + n) * G::kKPitch;
-        if constexpr (G::kBf16) {
-#pragma unroll
-          for (int s = 0; s < G::kQFrags; ++s)
-            sc[blk] = mfma_bf16_32x32x16(*(const bf16x8*)(krow + 16 * s + 8 * h2), qf[s], sc[blk]);
-        } else {
-#pragma unroll
-          for (int s = 0; s < G::kQFrags; ++s)
-            sc[blk] = mfma_f32_32x32x2(krow[2 * s + h2], qf[s], sc[blk]);
-        }
-      }
-      // mask only tiles crossing the diagonal or the window edge of this wave's tokens
-      const bool need_mask = (kb + kBN - 1 > tw0) || (W != 0 && kb <= tw1 - W);
-      if (need_mask) {
-#pragma unroll
-        for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-          for (int a = 0; a < 16; ++a) {
-            const int key = kb + 32 * blk + 8 * (a >> 2) + 4 * h2 + (a & 3);
-            const bool ok = key <= tq && (W == 0 || tq - key < W);
-            sc[blk][a] = ok ? sc[blk][a] : -INFINITY;
-          }
-      }
-      // online softmax (base 2, scale folded into c2)
-      float mx = -INFINITY;
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-        for (int a = 0; a < 16; ++a) mx = fmaxf(mx, sc[blk][a]);
-      mx = half_swap_max(mx) * c2;
-      // lazy rescale: the reference moves only when a score exceeds it by more than 2^8, so
-      // probabilities stay <= 256 and most tiles skip rescaling O (exact either way)
-      const bool move = mx > mref + kRescaleLog2;
-      if (__builtin_amdgcn_ballot_w64(move) != 0) {
-        const float mnew = move ? mx : mref;
-        // lanes that keep their reference scale by exactly 1 (also when it is still -inf)
-        const float alpha = move ? fast_exp2(mref - mnew) : 1.f;
-        l *= alpha;
-#pragma unroll
-        for (int d = 0; d < G::kDBlocks; ++d) o[d] *= alpha;
-        mref = mnew;
-      }
-      const float mu = mref == -INFINITY ? 0.f : mref;
-      float rs = 0.f;
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-        for (int a = 0; a < 16; ++a) {
-          const float e = fast_exp2(__builtin_fmaf(sc[blk][a], c2, -mu));
-          sc[blk][a] = e;
-          rs += e;
-        }
-      l += rs;
-
-      // O^T += V^T P^T
-      if constexpr (G::kBf16) {
-        const int j16 = lane & 15;
-        const int dh = (lane >> 4) & 1;
-#pragma unroll
-        for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-          for (int s = 0; s < 2; ++s) {
-            f32x8 pf;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) pf[e] = sc[blk][8 * s + e];
-            const bf16x8 pb = cvt_bf16x8(pf);
-            const int r0 = 32 * blk + 16 * s + 4 * h2 + (j16 >> 2);
-            const __bf16* v0 = (const __bf16*)Vs + r0 * G::kVPitch + 16 * dh + 4 * (j16 & 3);
-            const __bf16* v1 = v0 + 8 * G::kVPitch;
-#pragma unroll
-            for (int d = 0; d < G::kDBlocks; ++d) {
-              const bf16x4 lo4 = lds_read_tr4(v0 + 32 * d);
-              const bf16x4 hi4 = lds_read_tr4(v1 + 32 * d);
-              const bf16x8 va = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
-              o[d] = mfma_bf16_32x32x16(va, pb, o[d]);
-            }
-          }
-      } else {
-#pragma unroll
-        for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-          for (int u = 0; u < 16; ++u) {
-            const int key = 32 * blk + 8 * (u >> 2) + 4 * h2 + (u & 3);
-            const float* vr = (const float*)Vs + key * G::kVPitch + n;
-#pragma unroll
-            for (int d = 0; d < G::kDBlocks; ++d) o[d] = mfma_f32_32x32x2(vr[32 * d], sc[blk][u], o[d]);
-          }
-      }
-    }
-    if (j + 1 < n_tiles) stage_store((j + 1) & 1);
-    __syncthreads();
-  }
-
-  // ---- epilogue: combine half-wave sums, fold in the sink, normalise once, store
-  const float lt = half_swap_sum(l);
-  const float m2 = mref;  // reference max in log2 units (-inf if nothing was visible)
+// Half-wave sums combined, sink folded in, one normalisation, one rounding, LSE.
+template <typename T, int DB>
+__device__ __forceinline__ void epilogue(const DenseFwdParams& p, const Tile& w, const Cols& c,
+                                         const Softmax& st, const f32x16 (&o)[DB]) {
+  const float lt = half_swap_sum(st.l);
+  const float m2 = st.mref;  // reference max in log2 units (-inf if nothing was visible)
   float inv, lse_v;
   if (p.sinks != nullptr) {
-    const float s2 = p.sinks[hq] * kLog2e;
+    const float s2 = p.sinks[c.hq] * kLog2e;
     const float mm = fmaxf(m2, s2);
     const float corr = fast_exp2(m2 - mm);
     const float lf = lt * corr + fast_exp2(s2 - mm);
@@ -326,28 +264,419 @@ __global__ __launch_bounds__(kThreads, 2) void dense_fwd_kernel(DenseFwdParams p
     inv = 1.f / lt;
     lse_v = (m2 + __builtin_amdgcn_logf(lt)) * kLn2;
   }
-  if (tq < t_end) {
-    T* ob = (T*)p.out + (int64_t)tq * p.o_st + (int64_t)hq * p.o_sh;
+  if (c.tq < w.t_end) {
+    T* ob = (T*)p.out + (int64_t)c.tq * p.o_st + (int64_t)c.hq * p.o_sh;
 #pragma unroll
-    for (int d = 0; d < G::kDBlocks; ++d)
+    for (int d = 0; d < DB; ++d)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         f32x4 r;
 #pragma unroll
         for (int e = 0; e < 4; ++e) r[e] = o[d][4 * i + e] * inv;
-        T* dst = ob + 32 * d + 8 * i + 4 * h2;
-        if constexpr (G::kBf16) *(bf16x4*)dst = cvt_bf16x4(r);
+        T* dst = ob + 32 * d + 8 * i + 4 * c.h2;
+        if constexpr (std::is_same<T, __bf16>::value) *(bf16x4*)dst = cvt_bf16x4(r);
         else *(f32x4*)dst = r;
       }
-    if (p.lse != nullptr && h2 == 0) p.lse[(int64_t)tq * p.Hq + hq] = lse_v;
+    if (p.lse != nullptr && c.h2 == 0) p.lse[(int64_t)c.tq * p.Hq + c.hq] = lse_v;
   }
 }
 
-template <typename T, int D>
-hipError_t launch_one(const DenseFwdParams& p, hipStream_t stream) {
+// ======================================================================================
+// bf16: DMA-staged, software-pipelined kernel
+// ======================================================================================
+template <int D>
+struct Bf {
+  static constexpr int U = D / 8;                   // 16-byte units per row
+  static constexpr int kTileUnits = kBN * U;        // units per K (or V) tile
+  static constexpr int kDmaPerWave = kTileUnits / 64 / 4;
+  static constexpr int kQFrags = D / 16;
+  static constexpr int kDBlocks = D / 32;
+  static_assert(kTileUnits % 256 == 0, "tile must split evenly over the four waves");
+};
+
+// Physical 16-byte unit (within its row) of logical unit u is u ^ key(row).  K rows are
+// read 16 rows at one unit (MFMA A operand); V rows by ds_read_b64_tr_b16, 4 consecutive
+// rows x 4 consecutive units per half-wave.  With 64 banks of 4 bytes, a 256-byte bank line
+// holds one D=128 row or two D=64 rows.
+template <int D>
+__device__ __forceinline__ int k_key(int r) {
+  if constexpr (D == 128) return r & 15;
+  else return (r >> 1) & 7;
+}
+template <int D>
+__device__ __forceinline__ int v_key(int r) {
+  if constexpr (D == 128) return (r & 3) << 2;
+  else return ((r >> 1) & 1) << 2;
+}
+
+// Gather one 64-key tile (rows kb.. clamped to k_hi - 1) of one tensor into `buf` with
+// buffer_load ... lds (MUBUF LDS DMA: the tile base sits in the buffer descriptor, the
+// 64-unit block's row offset in soffset, so a transfer costs a few VALU).  Rows past the
+// tile's last query are clamped to the last valid row (always in bounds); every such key
+// lies after every valid query of the tile, so it is masked and contributes zero.
+template <int D, bool IS_V>
+__device__ __forceinline__ void dma_tile(const __bf16* base, int64_t st, int kb, int k_hi, u32x4* buf,
+                                         int wave, int lane_in) {
+  using B = Bf<D>;
+  constexpr int R = 64 / B::U;  // rows per 64-unit block
+  const int lane = opaque(lane_in);  // recomputed plan, nothing kept live across the loop
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(base + (int64_t)kb * st), (short)0, -1, kBufferWord3);
+  const uint32_t stb = (uint32_t)st * 2u;  // row stride in bytes (< 2^25)
+  const int lim = k_hi - 1 - kb;
+  const int lr = lane / B::U, lp = lane % B::U;
+  if (lim >= kBN - 1) {
+    const uint32_t lane_off = (uint32_t)lr * stb;
+#pragma unroll
+    for (int i = 0; i < B::kDmaPerWave; ++i) {
+      const int blk = i * 4 + wave;  // wave-uniform 64-unit block
+      const int r = blk * R + lr;
+      const int cu = lp ^ (IS_V ? v_key<D>(r) : k_key<D>(r));
+      u32x4* dst = buf + __builtin_amdgcn_readfirstlane(blk * 64);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)dst, 16, lane_off + (uint32_t)cu * 16u,
+                                               __builtin_amdgcn_readfirstlane((uint32_t)(blk * R) * stb), 0, 0);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < B::kDmaPerWave; ++i) {
+      const int blk = i * 4 + wave;
+      const int r = blk * R + lr;
+      const int cu = lp ^ (IS_V ? v_key<D>(r) : k_key<D>(r));
+      u32x4* dst = buf + __builtin_amdgcn_readfirstlane(blk * 64);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)dst, 16, (uint32_t)min(r, lim) * stb + (uint32_t)cu * 16u,
+                                               0, 0, 0);
+    }
+  }
+}
+
+// S^T for the two 32-key blocks of the tile in `kbuf`.
+template <int D>
+__device__ __forceinline__ void qk_tile(const u32x4* kbuf, const bf16x8 (&qf)[Bf<D>::kQFrags], int n_in, int h2,
+                                        f32x16 (&sc)[2]) {
+  using B = Bf<D>;
+  const int n = opaque(n_in);
+  const int kk = k_key<D>(n);  // equal for rows n and 32 + n
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk) {
+    sc[blk] = f32x16{};
+    const int row = (32 * blk + n) * B::U;
+#pragma unroll
+    for (int s = 0; s < B::kQFrags; ++s) {
+      const u32x4 a = kbuf[row + ((2 * s + h2) ^ kk)];
+      sc[blk] = mfma_bf16_32x32x16(__builtin_bit_cast(bf16x8, a), qf[s], sc[blk]);
+    }
+  }
+}
+
+// O^T += V^T P^T for the tile in `vbuf` (probabilities in sc).
+template <int D>
+__device__ __forceinline__ void pv_tile(const u32x4* vbuf, const f32x16 (&sc)[2], int lane_in,
+                                        f32x16 (&o)[Bf<D>::kDBlocks]) {
+  using B = Bf<D>;
+  const int lane = opaque(lane_in);
+  const int j16 = lane & 15, dh = (lane >> 4) & 1, h2 = lane >> 5;
+  const int vk = v_key<D>(j16 >> 2);  // rows 4*h2 + (j16 >> 2) (+16s, +32blk, +8): same key
+  const int sub = (j16 & 3) >> 1;
+  const int half = (j16 & 1) * 4;
+  const __bf16* elems = (const __bf16*)vbuf;
+  // one lane base per output block, taken as a single opaque index from the LDS buffer so
+  // every read stays a shallow GEP chain from it (and keeps the buffer's alias scope)
+  const __bf16* base[B::kDBlocks];
+#pragma unroll
+  for (int d = 0; d < B::kDBlocks; ++d)
+    base[d] = &elems[opaque(((4 * h2 + (j16 >> 2)) * B::U + ((4 * d + 2 * dh + sub) ^ vk)) * 8 + half)];
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      f32x8 pf;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pf[e] = sc[blk][8 * s + e];
+      const bf16x8 pb = cvt_bf16x8(pf);
+#pragma unroll
+      for (int d = 0; d < B::kDBlocks; ++d) {
+        const int row_off = (32 * blk + 16 * s) * B::U * 8;  // rows r0 and r0 + 8
+        const bf16x4 lo4 = lds_read_tr4(base[d] + row_off);
+        const bf16x4 hi4 = lds_read_tr4(base[d] + row_off + 8 * B::U * 8);
+        o[d] = mfma_bf16_32x32x16(__builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7), pb, o[d]);
+      }
+    }
+}
+
+// One pipelined step in program order: S(j) = K(j) Q^T on the MFMA unit while the
+// exponentials of tile j-1 run on the VALU, then O += V(j-1) P(j-1).  Operand fragments
+// stream from LDS kAhead MFMAs ahead of their use (K fragments first, then the transposed
+// V fragments), so each MFMA waits only for a read issued long before.  Every slot is
+// fenced with sched_barrier: the emitted order is exactly this one.
+template <int D>
+__device__ __forceinline__ float qk_pv_step(const u32x4* kbuf, const u32x4* vbuf, const bf16x8 (&qf)[Bf<D>::kQFrags],
+                                            int lane_in, int n_in, int h2, f32x16 (&sn)[2], const f32x16 (&sc)[2],
+                                            float c2, float mu, f32x16 (&o)[Bf<D>::kDBlocks], float& sn_max) {
+  using B = Bf<D>;
+  constexpr int NQ = 2 * B::kQFrags;  // QK^T MFMAs (16 for D = 128, 8 for D = 64)
+  constexpr int NP = 4 * B::kDBlocks; // PV MFMAs
+  constexpr int EPM = 32 / NQ;        // exponentials per QK^T MFMA slot
+  constexpr int kAhead = (D == 128) ? SWA_KAHEAD128 : 8;
+  const int n = opaque(n_in);
+  const int kk = k_key<D>(n);
+  const int lane = opaque(lane_in);
+  const int j16 = lane & 15, dh = (lane >> 4) & 1;
+  const int vk = v_key<D>(j16 >> 2);
+  const int sub = (j16 & 3) >> 1;
+  const int half = (j16 & 1) * 4;
+  const __bf16* elems = (const __bf16*)vbuf;
+  const __bf16* base[B::kDBlocks];
+#pragma unroll
+  for (int d = 0; d < B::kDBlocks; ++d)
+    base[d] = &elems[opaque(((4 * h2 + (j16 >> 2)) * B::U + ((4 * d + 2 * dh + sub) ^ vk)) * 8 + half)];
+
+  u32x4 frag[NQ + NP];
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): nothing older is in flight, later waits count exactly
+  auto read = [&](int f) {
+    if (f < NQ) {
+      const int blk = f & 1, s = f >> 1;  // the two key blocks alternate: neighbours are independent
+      frag[f] = kbuf[(32 * blk + n) * B::U + ((2 * s + h2) ^ kk)];
+    } else {
+      const int i = f - NQ, ks = i / B::kDBlocks, d = i % B::kDBlocks;
+      const int row_off = (32 * (ks >> 1) + 16 * (ks & 1)) * B::U * 8;  // rows r0 and r0 + 8
+      const bf16x4 lo4 = lds_read_tr4(base[d] + row_off);
+      const bf16x4 hi4 = lds_read_tr4(base[d] + row_off + 8 * B::U * 8);
+      frag[f] = __builtin_bit_cast(u32x4, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+  };
+#pragma unroll
+  for (int f = 0; f < kAhead; ++f) read(f);
+  __builtin_amdgcn_sched_barrier(0);
+
+  sn[0] = f32x16{};
+  sn[1] = f32x16{};
+  bf16x8 pb[4];
+  f32x8 pf;
+  float rs = 0.f;
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) {
+    sn[i & 1] = mfma_bf16_32x32x16(__builtin_bit_cast(bf16x8, frag[i]), qf[i >> 1], sn[i & 1]);
+    if (i + kAhead < NQ + NP) read(i + kAhead);
+#pragma unroll
+    for (int e = 0; e < EPM; ++e) {
+      const int x = i * EPM + e;  // element of tile j-1: block x / 16, accumulator x % 16
+      const float pe = fast_exp2(__builtin_fmaf(sc[x >> 4][x & 15], c2, -mu));
+      rs += pe;
+      pf[x & 7] = pe;
+      if ((x & 7) == 7) pb[x >> 3] = cvt_bf16x8(pf);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  constexpr int MPM = 16 / NP;  // max3 steps of the new scores per PV MFMA slot
+  float mx = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    const int ks = i / B::kDBlocks, d = i % B::kDBlocks;
+    o[d] = mfma_bf16_32x32x16(__builtin_bit_cast(bf16x8, frag[NQ + i]), pb[ks], o[d]);
+    if (NQ + i + kAhead < NQ + NP) read(NQ + i + kAhead);
+#pragma unroll
+    for (int e = 0; e < MPM; ++e) {
+      const int x = 2 * (i * MPM + e);
+      mx = __builtin_fmaxf(mx, __builtin_fmaxf(sn[x >> 4][x & 15], sn[x >> 4][(x & 15) + 1]));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  sn_max = mx;
+  return rs;
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void dense_fwd_bf16_kernel(DenseFwdParams p) {
+  using B = Bf<D>;
+  __shared__ u32x4 k0[B::kTileUnits];
+  __shared__ u32x4 k1[B::kTileUnits];
+  __shared__ u32x4 v0[B::kTileUnits];
+  __shared__ u32x4 v1[B::kTileUnits];
+
+  Tile w;
+  if (!decode_tile(p, w)) return;
+  if (w.padding) {
+    write_padding<__bf16, D>(p, w);
+    return;
+  }
+  const Cols c = make_cols(p, w);
+
+  bf16x8 qf[B::kQFrags];
+  {
+    const __bf16* qb = (const __bf16*)p.q + (int64_t)min(c.tq, w.t_end - 1) * p.q_st + (int64_t)c.hq * p.q_sh;
+#pragma unroll
+    for (int s = 0; s < B::kQFrags; ++s) qf[s] = *(const bf16x8*)(qb + 16 * s + 8 * c.h2);
+  }
+  const __bf16* kbase = (const __bf16*)p.k + (int64_t)w.g * p.k_sh;
+  const __bf16* vbase = (const __bf16*)p.v + (int64_t)w.g * p.v_sh;
+
+  f32x16 o[B::kDBlocks];
+#pragma unroll
+  for (int d = 0; d < B::kDBlocks; ++d) o[d] = f32x16{};
+  Softmax st{-INFINITY, 0.f};
+  const float c2 = p.c2;
+  const int nt = c.n_tiles;
+
+  // prologue: K(0) -> k0; then K(1) -> k1, V(0) -> v0 while S(0) is computed
+  dma_tile<D, false>(kbase, p.k_st, c.k_lo, c.k_hi, k0, c.wave, c.lane);
+  wait_vm0();
+  barrier_keep_loads();
+  if (nt > 1) dma_tile<D, false>(kbase, p.k_st, c.k_lo + kBN, c.k_hi, k1, c.wave, c.lane);
+  dma_tile<D, true>(vbase, p.v_st, c.k_lo, c.k_hi, v0, c.wave, c.lane);
+  f32x16 sc[2];
+  qk_tile<D>(k0, qf, c.n, c.h2, sc);
+  if (tile_needs_mask(c, c.k_lo)) mask_tile(sc, c.k_lo, c);
+  TileStats ts = tile_stats(lane_max(sc), c2, st);
+
+  // iteration j: S(j) from K(j) ; softmax + PV of tile j-1 ; K(j+1), V(j) in flight.
+  // On entry sc holds the masked scores of tile j-1 and ts their statistics.  After the
+  // rare O rescale, one fenced instruction stream runs the QK^T MFMAs of tile j with the
+  // exponentials of tile j-1 between them, masks tile j if it straddles the diagonal or
+  // the window edge, then runs the PV MFMAs of tile j-1 with the maximum of tile j between
+  // them.  Tiles a wave does not see are computed too: fully masked, they add nothing.
+  auto step = [&](int j, const u32x4* kcur, u32x4* knext, u32x4* vcur_dst, const u32x4* vprev) {
+    const int kb = c.k_lo + j * kBN;
+    wait_vm0();
+    barrier_keep_loads();  // K(j), V(j-1) landed for every wave; K(j-1), V(j-2) consumed
+    if (j + 1 < nt) dma_tile<D, false>(kbase, p.k_st, kb + kBN, c.k_hi, knext, c.wave, c.lane);
+    dma_tile<D, true>(vbase, p.v_st, kb, c.k_hi, vcur_dst, c.wave, c.lane);
+    rescale_o<B::kDBlocks>(ts.move, ts.alpha, o);
+    f32x16 sn[2];
+    float sn_max;
+    const float rs = qk_pv_step<D>(kcur, vprev, qf, c.lane, c.n, c.h2, sn, sc, c2, ts.mu, o, sn_max);
+    if (tile_needs_mask(c, kb)) {  // diagonal / window-edge tile: mask, then take the max again
+      mask_tile(sn, kb, c);
+      sn_max = lane_max(sn);
+    }
+    st.l = st.l * ts.alpha + rs;
+    ts = tile_stats(sn_max, c2, st);
+    sc[0] = sn[0];
+    sc[1] = sn[1];
+  };
+  int j = 1;
+  for (; j + 1 < nt; j += 2) {
+    step(j, k1, k0, v1, v0);
+    step(j + 1, k0, k1, v0, v1);
+  }
+  if (j < nt) step(j, k1, k0, v1, v0);
+  // last tile: its V is in buffer (nt - 1) & 1
+  wait_vm0();
+  barrier_keep_loads();
+  rescale_o<B::kDBlocks>(ts.move, ts.alpha, o);
+  st.l = st.l * ts.alpha + tile_exp(sc, c2, ts.mu);
+  if ((nt - 1) & 1) pv_tile<D>(v1, sc, c.lane, o);
+  else pv_tile<D>(v0, sc, c.lane, o);
+  epilogue<__bf16, B::kDBlocks>(p, w, c, st, o);
+}
+
+// ======================================================================================
+// fp32: register-staged kernel with padded LDS rows (parity path)
+// ======================================================================================
+template <int D>
+struct F32Geo {
+  static constexpr int kKPitch = D + 1;  // odd pitch: conflict-free scalar column reads
+  static constexpr int kVPitch = D;
+  static constexpr int kKElems = kBN * kKPitch;
+  static constexpr int kStage = kKElems + kBN * kVPitch;
+  static constexpr int kQFrags = D / 2;
+  static constexpr int kDBlocks = D / 32;
+  static constexpr int kChunksPerRow = D / 4;
+  static constexpr int kLoads = kBN * kChunksPerRow / kThreads;
+};
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 1) void dense_fwd_f32_kernel(DenseFwdParams p) {
+  using G = F32Geo<D>;
+  __shared__ __attribute__((aligned(16))) float smem[2 * G::kStage];
+  Tile w;
+  if (!decode_tile(p, w)) return;
+  if (w.padding) {
+    write_padding<float, D>(p, w);
+    return;
+  }
+  const Cols c = make_cols(p, w);
+  float qf[G::kQFrags];
+  {
+    const float* qb = (const float*)p.q + (int64_t)min(c.tq, w.t_end - 1) * p.q_st + (int64_t)c.hq * p.q_sh;
+#pragma unroll
+    for (int s = 0; s < G::kQFrags; ++s) qf[s] = qb[2 * s + c.h2];
+  }
+  const float* kbase = (const float*)p.k + (int64_t)w.g * p.k_sh;
+  const float* vbase = (const float*)p.v + (int64_t)w.g * p.v_sh;
+  u32x4 kreg[G::kLoads], vreg[G::kLoads];
+  // rows past the tile's last query are clamped to the last valid row; they are masked
+  auto stage_load = [&](int kb) {
+    const int lim = c.k_hi - 1 - kb;
+#pragma unroll
+    for (int i = 0; i < G::kLoads; ++i) {
+      const int e = threadIdx.x + i * kThreads;
+      const int row = min(e / G::kChunksPerRow, lim);
+      const int col = (e % G::kChunksPerRow) * 4;
+      kreg[i] = *(const u32x4*)(kbase + (int64_t)(kb + row) * p.k_st + col);
+      vreg[i] = *(const u32x4*)(vbase + (int64_t)(kb + row) * p.v_st + col);
+    }
+  };
+  auto stage_store = [&](int buf) {
+    float* Ks = smem + buf * G::kStage;
+    float* Vs = Ks + G::kKElems;
+#pragma unroll
+    for (int i = 0; i < G::kLoads; ++i) {
+      const int e = threadIdx.x + i * kThreads;
+      const int row = e / G::kChunksPerRow;
+      const int col = (e % G::kChunksPerRow) * 4;
+      float* kd = Ks + row * G::kKPitch + col;
+      kd[0] = __uint_as_float(kreg[i][0]);
+      kd[1] = __uint_as_float(kreg[i][1]);
+      kd[2] = __uint_as_float(kreg[i][2]);
+      kd[3] = __uint_as_float(kreg[i][3]);
+      *(u32x4*)(Vs + row * G::kVPitch + col) = vreg[i];
+    }
+  };
+  f32x16 o[G::kDBlocks];
+#pragma unroll
+  for (int d = 0; d < G::kDBlocks; ++d) o[d] = f32x16{};
+  Softmax st{-INFINITY, 0.f};
+  if (c.n_tiles > 0) {
+    stage_load(c.k_lo);
+    stage_store(0);
+  }
+  __syncthreads();
+  for (int j = 0; j < c.n_tiles; ++j) {
+    const int kb = c.k_lo + j * kBN;
+    if (j + 1 < c.n_tiles) stage_load(kb + kBN);
+    const float* Ks = smem + (j & 1) * G::kStage;
+    const float* Vs = Ks + G::kKElems;
+    if (tile_active(c, kb)) {
+      f32x16 sc[2];
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk) {
+        sc[blk] = f32x16{};
+        const float* krow = Ks + (32 * blk + c.n) * G::kKPitch;
+#pragma unroll
+        for (int s = 0; s < G::kQFrags; ++s) sc[blk] = mfma_f32_32x32x2(krow[2 * s + c.h2], qf[s], sc[blk]);
+      }
+      softmax_tile<G::kDBlocks>(sc, tile_needs_mask(c, kb), kb, c, p.c2, st, o);
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          const int key = 32 * blk + 8 * (u >> 2) + 4 * c.h2 + (u & 3);
+          const float* vr = Vs + key * G::kVPitch + c.n;
+#pragma unroll
+          for (int d = 0; d < G::kDBlocks; ++d) o[d] = mfma_f32_32x32x2(vr[32 * d], sc[blk][u], o[d]);
+        }
+    }
+    if (j + 1 < c.n_tiles) stage_store((j + 1) & 1);
+    __syncthreads();
+  }
+  epilogue<float, G::kDBlocks>(p, w, c, st, o);
+}
+
+template <typename K>
+hipError_t launch_kernel(K kernel, const DenseFwdParams& p, hipStream_t stream) {
   const int64_t grid = dense_fwd_grid(p);
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL((dense_fwd_kernel<T, D>), dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -375,11 +704,11 @@ int64_t dense_fwd_grid(const DenseFwdParams& p) {
 
 hipError_t dense_fwd_launch(const DenseFwdParams& p, Dtype dt, int D, hipStream_t stream) {
   if (dt == Dtype::BF16) {
-    if (D == 128) return launch_one<__bf16, 128>(p, stream);
-    if (D == 64) return launch_one<__bf16, 64>(p, stream);
+    if (D == 128) return launch_kernel(dense_fwd_bf16_kernel<128>, p, stream);
+    if (D == 64) return launch_kernel(dense_fwd_bf16_kernel<64>, p, stream);
   } else {
-    if (D == 128) return launch_one<float, 128>(p, stream);
-    if (D == 64) return launch_one<float, 64>(p, stream);
+    if (D == 128) return launch_kernel(dense_fwd_f32_kernel<128>, p, stream);
+    if (D == 64) return launch_kernel(dense_fwd_f32_kernel<64>, p, stream);
   }
   return hipErrorInvalidValue;
 }
