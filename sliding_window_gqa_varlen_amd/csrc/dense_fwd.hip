@@ -50,11 +50,18 @@ constexpr int kBN = 64;    // keys per tile
 constexpr int kXcds = 8;   // MI355X: workgroups are dealt round-robin to 8 XCDs
 constexpr float kRescaleLog2 = 8.f;  // lazy-rescale threshold (log2 units)
 #ifndef SWA_KAHEAD128
-#define SWA_KAHEAD128 4
+#define SWA_KAHEAD128 8
+#endif
+#ifndef SWA_KAHEAD64
+#define SWA_KAHEAD64 4
+#endif
+#ifndef SWA_OCC64
+#define SWA_OCC64 3
 #endif
 
 typedef __attribute__((address_space(3))) void lds_void;
 constexpr int kBufferWord3 = 0x00020000;  // buffer descriptor word 3: 32-bit data format, raw access
+
 typedef __attribute__((address_space(1))) const void glob_cvoid;
 
 // s_waitcnt vmcnt(0) with expcnt / lgkmcnt unconstrained
@@ -416,9 +423,12 @@ __device__ __forceinline__ float qk_pv_step(const u32x4* kbuf, const u32x4* vbuf
   constexpr int NQ = 2 * B::kQFrags;  // QK^T MFMAs (16 for D = 128, 8 for D = 64)
   constexpr int NP = 4 * B::kDBlocks; // PV MFMAs
   constexpr int EPM = 32 / NQ;        // exponentials per QK^T MFMA slot
-  constexpr int kAhead = (D == 128) ? SWA_KAHEAD128 : 8;
+  constexpr int kAhead = (D == 128) ? SWA_KAHEAD128 : SWA_KAHEAD64;
   const int n = opaque(n_in);
-  const int kk = k_key<D>(n);
+  // K fragment (key block blk, k-step s) of this lane: row 32 blk + n, 16-byte unit
+  // (2 s + h2) ^ key(n).  The row base has zero unit bits, so the byte address is
+  // kaddr ^ (32 s) (+ blk * 32 rows as an immediate offset) with kaddr = row | unit(s = 0).
+  const int kaddr = opaque(n * B::U * 16 + ((h2 ^ k_key<D>(n)) << 4));
   const int lane = opaque(lane_in);
   const int j16 = lane & 15, dh = (lane >> 4) & 1;
   const int vk = v_key<D>(j16 >> 2);
@@ -435,7 +445,7 @@ __device__ __forceinline__ float qk_pv_step(const u32x4* kbuf, const u32x4* vbuf
   auto read = [&](int f) {
     if (f < NQ) {
       const int blk = f & 1, s = f >> 1;  // the two key blocks alternate: neighbours are independent
-      frag[f] = kbuf[(32 * blk + n) * B::U + ((2 * s + h2) ^ kk)];
+      frag[f] = *(const u32x4*)((const char*)kbuf + (kaddr ^ (32 * s)) + blk * 32 * B::U * 16);
     } else {
       const int i = f - NQ, ks = i / B::kDBlocks, d = i % B::kDBlocks;
       const int row_off = (32 * (ks >> 1) + 16 * (ks & 1)) * B::U * 8;  // rows r0 and r0 + 8
@@ -460,13 +470,16 @@ __device__ __forceinline__ float qk_pv_step(const u32x4* kbuf, const u32x4* vbuf
 #pragma unroll
     for (int e = 0; e < EPM; ++e) {
       const int x = i * EPM + e;  // element of tile j-1: block x / 16, accumulator x % 16
-      const float pe = fast_exp2(__builtin_fmaf(sc[x >> 4][x & 15], c2, -mu));
-      rs += pe;
-      pf[x & 7] = pe;
-      if ((x & 7) == 7) pb[x >> 3] = cvt_bf16x8(pf);
+      pf[x & 7] = fast_exp2(__builtin_fmaf(sc[x >> 4][x & 15], c2, -mu));
+      if ((x & 7) == 7) {
+        pb[x >> 3] = cvt_bf16x8(pf);
+#pragma unroll
+        for (int h = 0; h < 8; ++h) rs += pf[h];
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
   }
+  asm volatile("" ::"v"(rs));  // the row sum is finished inside the stream
   constexpr int MPM = 16 / NP;  // max3 steps of the new scores per PV MFMA slot
   float mx = -INFINITY;
 #pragma unroll
@@ -477,7 +490,8 @@ __device__ __forceinline__ float qk_pv_step(const u32x4* kbuf, const u32x4* vbuf
 #pragma unroll
     for (int e = 0; e < MPM; ++e) {
       const int x = 2 * (i * MPM + e);
-      mx = __builtin_fmaxf(mx, __builtin_fmaxf(sn[x >> 4][x & 15], sn[x >> 4][(x & 15) + 1]));
+      mx = fmaxf(mx, sn[x >> 4][x & 15]);
+      mx = fmaxf(mx, sn[x >> 4][(x & 15) + 1]);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -486,7 +500,7 @@ __device__ __forceinline__ float qk_pv_step(const u32x4* kbuf, const u32x4* vbuf
 }
 
 template <int D>
-__global__ __launch_bounds__(kThreads, 2) void dense_fwd_bf16_kernel(DenseFwdParams p) {
+__global__ __launch_bounds__(kThreads, D == 64 ? SWA_OCC64 : 2) void dense_fwd_bf16_kernel(DenseFwdParams p) {
   using B = Bf<D>;
   __shared__ u32x4 k0[B::kTileUnits];
   __shared__ u32x4 k1[B::kTileUnits];
