@@ -150,8 +150,8 @@ def cpu_baseline_sparse(inp, budget_s: float = 20.0) -> dict:
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="causal_gqa_bf16_t8192",
                     choices=[w.name for w in W.WORKLOADS])
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -61,6 +61,8 @@ constexpr float kRescaleLog2 = 8.f;  // lazy-rescale threshold (log2 units)
 
 typedef __attribute__((address_space(3))) void lds_void;
 constexpr int kBufferWord3 = 0x00020000;  // buffer descriptor word 3: 32-bit data format, raw access
+constexpr bf16x8 kOnesBf16x8 = {(__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f,
+                                (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f};
 
 typedef __attribute__((address_space(1))) const void glob_cvoid;
 
@@ -242,6 +244,14 @@ __device__ __forceinline__ void rescale_o(bool move, float alpha, f32x16 (&o)[DB
     for (int d = 0; d < DB; ++d) o[d] *= alpha;
   }
 }
+template <int DB>
+__device__ __forceinline__ void rescale_o(bool move, float alpha, f32x16 (&o)[DB], f32x16& lacc) {
+  if (__builtin_amdgcn_ballot_w64(move) != 0) {
+#pragma unroll
+    for (int d = 0; d < DB; ++d) o[d] *= alpha;
+    lacc *= alpha;
+  }
+}
 
 // Full online-softmax step for one tile (used where nothing is interleaved with it).
 template <int DB>
@@ -254,10 +264,11 @@ __device__ __forceinline__ void softmax_tile(f32x16 (&sc)[2], bool need_mask, in
 }
 
 // Half-wave sums combined, sink folded in, one normalisation, one rounding, LSE.
+// `st.l` holds this half-wave's share of the row sum, or the whole sum if `full_sum`.
 template <typename T, int DB>
 __device__ __forceinline__ void epilogue(const DenseFwdParams& p, const Tile& w, const Cols& c,
-                                         const Softmax& st, const f32x16 (&o)[DB]) {
-  const float lt = half_swap_sum(st.l);
+                                         const Softmax& st, const f32x16 (&o)[DB], bool full_sum = false) {
+  const float lt = full_sum ? st.l : half_swap_sum(st.l);
   const float m2 = st.mref;  // reference max in log2 units (-inf if nothing was visible)
   float inv, lse_v;
   if (p.sinks != nullptr) {
@@ -298,6 +309,8 @@ struct Bf {
   static constexpr int kDmaPerWave = kTileUnits / 64 / 4;
   static constexpr int kQFrags = D / 16;
   static constexpr int kDBlocks = D / 32;
+  // row sums on the MFMA unit (an extra all-ones block of V^T) where registers allow
+  static constexpr bool kMfmaRowSum = D == 128;
   static_assert(kTileUnits % 256 == 0, "tile must split evenly over the four waves");
 };
 
@@ -375,39 +388,52 @@ __device__ __forceinline__ void qk_tile(const u32x4* kbuf, const bf16x8 (&qf)[Bf
   }
 }
 
-// O^T += V^T P^T for the tile in `vbuf` (probabilities in sc).
+// Byte offsets, within a V tile, of this lane's ds_read_b64_tr_b16 for each output block
+// (rows 4 h2 + (lane & 15) / 4, 16-byte units 4 d + 2 dh + sub, XOR-swizzled); the k-step
+// rows and the +8-row half are immediate offsets on top.
 template <int D>
-__device__ __forceinline__ void pv_tile(const u32x4* vbuf, const f32x16 (&sc)[2], int lane_in,
-                                        f32x16 (&o)[Bf<D>::kDBlocks]) {
+struct VOffsets {
+  int off[Bf<D>::kDBlocks];
+};
+template <int D>
+__device__ __forceinline__ VOffsets<D> v_offsets(int lane) {
   using B = Bf<D>;
-  const int lane = opaque(lane_in);
   const int j16 = lane & 15, dh = (lane >> 4) & 1, h2 = lane >> 5;
   const int vk = v_key<D>(j16 >> 2);  // rows 4*h2 + (j16 >> 2) (+16s, +32blk, +8): same key
   const int sub = (j16 & 3) >> 1;
   const int half = (j16 & 1) * 4;
-  const __bf16* elems = (const __bf16*)vbuf;
-  // one lane base per output block, taken as a single opaque index from the LDS buffer so
-  // every read stays a shallow GEP chain from it (and keeps the buffer's alias scope)
-  const __bf16* base[B::kDBlocks];
+  VOffsets<D> v;
 #pragma unroll
   for (int d = 0; d < B::kDBlocks; ++d)
-    base[d] = &elems[opaque(((4 * h2 + (j16 >> 2)) * B::U + ((4 * d + 2 * dh + sub) ^ vk)) * 8 + half)];
+    v.off[d] = (((4 * h2 + (j16 >> 2)) * B::U + ((4 * d + 2 * dh + sub) ^ vk)) * 8 + half) * 2;
+  return v;
+}
+template <int D>
+__device__ __forceinline__ bf16x8 v_frag(const u32x4* vbuf, const VOffsets<D>& vo, int ks, int d) {
+  using B = Bf<D>;
+  const int row_off = (32 * (ks >> 1) + 16 * (ks & 1)) * B::U * 16;  // rows r0 and r0 + 8
+  const char* p = (const char*)vbuf + vo.off[d] + row_off;
+  const bf16x4 lo4 = lds_read_tr4((const __bf16*)p);
+  const bf16x4 hi4 = lds_read_tr4((const __bf16*)(p + 8 * B::U * 16));
+  return __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// O^T += V^T P^T for the tile in `vbuf` (probabilities in sc); with the MFMA row sum,
+// lacc += 1 P^T as well.
+template <int D>
+__device__ __forceinline__ void pv_tile(const u32x4* vbuf, const f32x16 (&sc)[2], const VOffsets<D>& vo,
+                                        f32x16 (&o)[Bf<D>::kDBlocks], f32x16& lacc) {
+  using B = Bf<D>;
 #pragma unroll
-  for (int blk = 0; blk < 2; ++blk)
+  for (int ks = 0; ks < 4; ++ks) {
+    f32x8 pf;
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      f32x8 pf;
+    for (int e = 0; e < 8; ++e) pf[e] = sc[ks >> 1][8 * (ks & 1) + e];
+    const bf16x8 pb = cvt_bf16x8(pf);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pf[e] = sc[blk][8 * s + e];
-      const bf16x8 pb = cvt_bf16x8(pf);
-#pragma unroll
-      for (int d = 0; d < B::kDBlocks; ++d) {
-        const int row_off = (32 * blk + 16 * s) * B::U * 8;  // rows r0 and r0 + 8
-        const bf16x4 lo4 = lds_read_tr4(base[d] + row_off);
-        const bf16x4 hi4 = lds_read_tr4(base[d] + row_off + 8 * B::U * 8);
-        o[d] = mfma_bf16_32x32x16(__builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7), pb, o[d]);
-      }
-    }
+    for (int d = 0; d < B::kDBlocks; ++d) o[d] = mfma_bf16_32x32x16(v_frag<D>(vbuf, vo, ks, d), pb, o[d]);
+    if constexpr (B::kMfmaRowSum) lacc = mfma_bf16_32x32x16(kOnesBf16x8, pb, lacc);
+  }
 }
 
 // One pipelined step in program order: S(j) = K(j) Q^T on the MFMA unit while the
@@ -417,41 +443,24 @@ __device__ __forceinline__ void pv_tile(const u32x4* vbuf, const f32x16 (&sc)[2]
 // fenced with sched_barrier: the emitted order is exactly this one.
 template <int D>
 __device__ __forceinline__ float qk_pv_step(const u32x4* kbuf, const u32x4* vbuf, const bf16x8 (&qf)[Bf<D>::kQFrags],
-                                            int lane_in, int n_in, int h2, f32x16 (&sn)[2], const f32x16 (&sc)[2],
-                                            float c2, float mu, f32x16 (&o)[Bf<D>::kDBlocks], float& sn_max) {
+                                            int kaddr, const VOffsets<D>& vo, f32x16 (&sn)[2],
+                                            const f32x16 (&sc)[2], float c2, float mu, f32x16 (&o)[Bf<D>::kDBlocks],
+                                            f32x16& lacc, float& sn_max) {
   using B = Bf<D>;
   constexpr int NQ = 2 * B::kQFrags;  // QK^T MFMAs (16 for D = 128, 8 for D = 64)
   constexpr int NP = 4 * B::kDBlocks; // PV MFMAs
   constexpr int EPM = 32 / NQ;        // exponentials per QK^T MFMA slot
   constexpr int kAhead = (D == 128) ? SWA_KAHEAD128 : SWA_KAHEAD64;
-  const int n = opaque(n_in);
-  // K fragment (key block blk, k-step s) of this lane: row 32 blk + n, 16-byte unit
-  // (2 s + h2) ^ key(n).  The row base has zero unit bits, so the byte address is
-  // kaddr ^ (32 s) (+ blk * 32 rows as an immediate offset) with kaddr = row | unit(s = 0).
-  const int kaddr = opaque(n * B::U * 16 + ((h2 ^ k_key<D>(n)) << 4));
-  const int lane = opaque(lane_in);
-  const int j16 = lane & 15, dh = (lane >> 4) & 1;
-  const int vk = v_key<D>(j16 >> 2);
-  const int sub = (j16 & 3) >> 1;
-  const int half = (j16 & 1) * 4;
-  const __bf16* elems = (const __bf16*)vbuf;
-  const __bf16* base[B::kDBlocks];
-#pragma unroll
-  for (int d = 0; d < B::kDBlocks; ++d)
-    base[d] = &elems[opaque(((4 * h2 + (j16 >> 2)) * B::U + ((4 * d + 2 * dh + sub) ^ vk)) * 8 + half)];
-
   u32x4 frag[NQ + NP];
+  __builtin_amdgcn_s_setprio(1);  // the wave in its MFMA stream goes first
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): nothing older is in flight, later waits count exactly
   auto read = [&](int f) {
     if (f < NQ) {
       const int blk = f & 1, s = f >> 1;  // the two key blocks alternate: neighbours are independent
       frag[f] = *(const u32x4*)((const char*)kbuf + (kaddr ^ (32 * s)) + blk * 32 * B::U * 16);
     } else {
-      const int i = f - NQ, ks = i / B::kDBlocks, d = i % B::kDBlocks;
-      const int row_off = (32 * (ks >> 1) + 16 * (ks & 1)) * B::U * 8;  // rows r0 and r0 + 8
-      const bf16x4 lo4 = lds_read_tr4(base[d] + row_off);
-      const bf16x4 hi4 = lds_read_tr4(base[d] + row_off + 8 * B::U * 8);
-      frag[f] = __builtin_bit_cast(u32x4, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+      const int i = f - NQ;
+      frag[f] = __builtin_bit_cast(u32x4, v_frag<D>(vbuf, vo, i / B::kDBlocks, i % B::kDBlocks));
     }
   };
 #pragma unroll
@@ -471,21 +480,27 @@ __device__ __forceinline__ float qk_pv_step(const u32x4* kbuf, const u32x4* vbuf
     for (int e = 0; e < EPM; ++e) {
       const int x = i * EPM + e;  // element of tile j-1: block x / 16, accumulator x % 16
       pf[x & 7] = fast_exp2(__builtin_fmaf(sc[x >> 4][x & 15], c2, -mu));
+      asm volatile("" : "+v"(pf[x & 7]));  // this slot's exponentials stay in this slot
       if ((x & 7) == 7) {
         pb[x >> 3] = cvt_bf16x8(pf);
+        if constexpr (!B::kMfmaRowSum) {
 #pragma unroll
-        for (int h = 0; h < 8; ++h) rs += pf[h];
+          for (int h = 0; h < 8; ++h) rs += pf[h];
+        }
       }
     }
     __builtin_amdgcn_sched_barrier(0);
   }
-  asm volatile("" ::"v"(rs));  // the row sum is finished inside the stream
+  if constexpr (!B::kMfmaRowSum) asm volatile("" ::"v"(rs));  // the row sum is finished inside the stream
   constexpr int MPM = 16 / NP;  // max3 steps of the new scores per PV MFMA slot
   float mx = -INFINITY;
 #pragma unroll
   for (int i = 0; i < NP; ++i) {
     const int ks = i / B::kDBlocks, d = i % B::kDBlocks;
     o[d] = mfma_bf16_32x32x16(__builtin_bit_cast(bf16x8, frag[NQ + i]), pb[ks], o[d]);
+    if constexpr (B::kMfmaRowSum) {
+      if (d == B::kDBlocks - 1) lacc = mfma_bf16_32x32x16(kOnesBf16x8, pb[ks], lacc);
+    }
     if (NQ + i + kAhead < NQ + NP) read(NQ + i + kAhead);
 #pragma unroll
     for (int e = 0; e < MPM; ++e) {
@@ -493,9 +508,11 @@ __device__ __forceinline__ float qk_pv_step(const u32x4* kbuf, const u32x4* vbuf
       mx = fmaxf(mx, sn[x >> 4][x & 15]);
       mx = fmaxf(mx, sn[x >> 4][(x & 15) + 1]);
     }
+    asm volatile("" : "+v"(mx));  // keeps this slot's share of the maximum in this slot
     __builtin_amdgcn_sched_barrier(0);
   }
   sn_max = mx;
+  __builtin_amdgcn_s_setprio(0);
   return rs;
 }
 
@@ -527,9 +544,14 @@ __global__ __launch_bounds__(kThreads, D == 64 ? SWA_OCC64 : 2) void dense_fwd_b
   f32x16 o[B::kDBlocks];
 #pragma unroll
   for (int d = 0; d < B::kDBlocks; ++d) o[d] = f32x16{};
+  f32x16 lacc = f32x16{};  // MFMA row sums (every row holds the column's sum)
   Softmax st{-INFINITY, 0.f};
   const float c2 = p.c2;
   const int nt = c.n_tiles;
+  // loop-invariant LDS byte offsets of this lane's K and V fragments: K row n, unit
+  // (2 s + h2) ^ key(n) = (h2 ^ key(n)) ^ 2 s, so the address is kaddr ^ (32 s)
+  const int kaddr = c.n * B::U * 16 + ((c.h2 ^ k_key<D>(c.n)) << 4);
+  const VOffsets<D> vo = v_offsets<D>(c.lane);
 
   // prologue: K(0) -> k0; then K(1) -> k1, V(0) -> v0 while S(0) is computed
   dma_tile<D, false>(kbase, p.k_st, c.k_lo, c.k_hi, k0, c.wave, c.lane);
@@ -554,10 +576,10 @@ __global__ __launch_bounds__(kThreads, D == 64 ? SWA_OCC64 : 2) void dense_fwd_b
     barrier_keep_loads();  // K(j), V(j-1) landed for every wave; K(j-1), V(j-2) consumed
     if (j + 1 < nt) dma_tile<D, false>(kbase, p.k_st, kb + kBN, c.k_hi, knext, c.wave, c.lane);
     dma_tile<D, true>(vbase, p.v_st, kb, c.k_hi, vcur_dst, c.wave, c.lane);
-    rescale_o<B::kDBlocks>(ts.move, ts.alpha, o);
+    rescale_o<B::kDBlocks>(ts.move, ts.alpha, o, lacc);
     f32x16 sn[2];
     float sn_max;
-    const float rs = qk_pv_step<D>(kcur, vprev, qf, c.lane, c.n, c.h2, sn, sc, c2, ts.mu, o, sn_max);
+    const float rs = qk_pv_step<D>(kcur, vprev, qf, kaddr, vo, sn, sc, c2, ts.mu, o, lacc, sn_max);
     if (tile_needs_mask(c, kb)) {  // diagonal / window-edge tile: mask, then take the max again
       mask_tile(sn, kb, c);
       sn_max = lane_max(sn);
@@ -576,11 +598,12 @@ __global__ __launch_bounds__(kThreads, D == 64 ? SWA_OCC64 : 2) void dense_fwd_b
   // last tile: its V is in buffer (nt - 1) & 1
   wait_vm0();
   barrier_keep_loads();
-  rescale_o<B::kDBlocks>(ts.move, ts.alpha, o);
+  rescale_o<B::kDBlocks>(ts.move, ts.alpha, o, lacc);
   st.l = st.l * ts.alpha + tile_exp(sc, c2, ts.mu);
-  if ((nt - 1) & 1) pv_tile<D>(v1, sc, c.lane, o);
-  else pv_tile<D>(v0, sc, c.lane, o);
-  epilogue<__bf16, B::kDBlocks>(p, w, c, st, o);
+  if ((nt - 1) & 1) pv_tile<D>(v1, sc, vo, o, lacc);
+  else pv_tile<D>(v0, sc, vo, o, lacc);
+  if constexpr (B::kMfmaRowSum) st.l = lacc[0];
+  epilogue<__bf16, B::kDBlocks>(p, w, c, st, o, B::kMfmaRowSum);
 }
 
 // ======================================================================================
