@@ -181,6 +181,10 @@ int32_t sparse_mla_fwd(const swa_tensor* q, const swa_tensor* latent, const swa_
   if (T > 0 && (same_data(out, q) || same_data(out, latent) || same_data(out, k_pe)))
     return fail(SWA_ERR_ARG, "out must not alias an input");
   if (T == 0) return SWA_OK;
+  // the gathers address both tensors with 32-bit byte offsets from their bases
+  if ((T - 1) * latent->stride[0] * 2 + 1024 > (int64_t)UINT32_MAX ||
+      (T - 1) * k_pe->stride[0] * 2 + 128 > (int64_t)UINT32_MAX)
+    return fail(SWA_ERR_UNSUPPORTED, "latent or k_pe spans more than 4 GiB");
 
   swa::SparseMlaParams p{};
   p.q = q->data;

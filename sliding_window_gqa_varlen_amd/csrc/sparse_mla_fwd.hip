@@ -65,7 +65,7 @@ __device__ __forceinline__ int lat_key(int r) { return ((r & 3) << 2) | ((r >> 2
 __device__ __forceinline__ int rope_key(int r) { return (r >> 1) & 7; }
 
 typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(1))) const void glob_cvoid;
+constexpr int kBufferWord3 = 0x00020000;  // buffer descriptor word 3: 32-bit data format, raw access
 
 // s_waitcnt vmcnt(N) with expcnt / lgkmcnt unconstrained
 template <int N>
@@ -92,8 +92,13 @@ struct Lane {
 // Slots past the compacted count (and whole chunks past the end) read the token's own row.
 __device__ __forceinline__ void gather_chunk(const SparseMlaParams& p, const int32_t* s_idx, int nv, int chunk,
                                              int t, u32x4* buf, const Lane& L) {
-  const __bf16* lat = (const __bf16*)p.latent;
-  const __bf16* kpe = (const __bf16*)p.k_pe;
+  // MUBUF LDS DMA (buffer_load ... lds): byte offsets from the tensor bases (the host
+  // checks that both tensors fit 32-bit offsets).  Unlike the FLAT form, pending buffer
+  // transfers leave the LDS read counters exact, so LDS reads below wait only for
+  // themselves.
+  const __amdgpu_buffer_rsrc_t lat = __builtin_amdgcn_make_buffer_rsrc((void*)p.latent, (short)0, -1, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t kpe = __builtin_amdgcn_make_buffer_rsrc((void*)p.k_pe, (short)0, -1, kBufferWord3);
+  const uint32_t lat_stb = (uint32_t)p.lat_st * 2u, kpe_stb = (uint32_t)p.kpe_st * 2u;
   // recompute the per-lane gather plan here instead of keeping it live across the loop
   int lane = L.lane;
   asm volatile("" : "+v"(lane));
@@ -106,8 +111,8 @@ __device__ __forceinline__ void gather_chunk(const SparseMlaParams& p, const int
     const int slot = chunk * kSlots + r;
     const int idx = slot < nv ? s_idx[slot] : t;
     u32x4* dst = buf + __builtin_amdgcn_readfirstlane(blk * 64);
-    __builtin_amdgcn_global_load_lds((glob_cvoid*)(lat + (int64_t)idx * p.lat_st + piece * 8), (lds_void*)dst,
-                                     16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(lat, (lds_void*)dst, 16, (uint32_t)idx * lat_stb + (uint32_t)piece * 16u,
+                                             0, 0, 0);
   }
 #pragma unroll
   for (int i = 0; i < kRopeDma; ++i) {
@@ -118,8 +123,9 @@ __device__ __forceinline__ void gather_chunk(const SparseMlaParams& p, const int
     const int slot = chunk * kSlots + r;
     const int idx = slot < nv ? s_idx[slot] : t;
     uint32_t* dst = (uint32_t*)(buf + kLatRegion) + __builtin_amdgcn_readfirstlane(blk * 64);
-    __builtin_amdgcn_global_load_lds((glob_cvoid*)(kpe + (int64_t)idx * p.kpe_st + unit * 8 + (dw & 3) * 2),
-                                     (lds_void*)dst, 4, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(kpe, (lds_void*)dst, 4,
+                                             (uint32_t)idx * kpe_stb + (uint32_t)unit * 16u + (uint32_t)(dw & 3) * 4u, 0, 0,
+                                             0);
   }
 }
 
