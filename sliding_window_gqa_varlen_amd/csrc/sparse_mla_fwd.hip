@@ -25,11 +25,11 @@
 #include "device_common.h"
 #include "launch.h"
 
-#ifndef SWA_SPARSE_QGROUP
-#define SWA_SPARSE_QGROUP 6
+#ifndef SWA_SPARSE_QAHEAD
+#define SWA_SPARSE_QAHEAD 3
 #endif
-#ifndef SWA_SPARSE_PVGROUP
-#define SWA_SPARSE_PVGROUP 2
+#ifndef SWA_SPARSE_PVAHEAD
+#define SWA_SPARSE_PVAHEAD 2
 #endif
 
 namespace swa {
@@ -51,8 +51,8 @@ constexpr int kSlotsPerThread = kSeg / kThreads;    // 4
 constexpr int kQFrags = 18;                         // k-steps of 16 coordinates per wave
 constexpr int kDBlocks = 8;                         // 256 output coordinates per wave / 32
 constexpr float kRescaleLog2 = 8.f;                 // lazy-rescale threshold (log2 units)
-constexpr int kQGroup = SWA_SPARSE_QGROUP;          // k-steps between scheduling fences
-constexpr int kPvGroup = SWA_SPARSE_PVGROUP;        // output blocks between scheduling fences
+constexpr int kQAhead = SWA_SPARSE_QAHEAD;          // QK^T fragments read ahead of their MFMA
+constexpr int kPvAhead = SWA_SPARSE_PVAHEAD;        // PV fragments read ahead of their MFMA
 static_assert(kLatRegion % (64 * kWaves) == 0 && (kSlots * kRopeUnits * 4) % (64 * kWaves) == 0,
               "every wave issues the same number of gathers");
 
@@ -102,30 +102,28 @@ __device__ __forceinline__ void gather_chunk(const SparseMlaParams& p, const int
   // recompute the per-lane gather plan here instead of keeping it live across the loop
   int lane = L.lane;
   asm volatile("" : "+v"(lane));
+  // lane l < 32 reads the index of slot row l once; each transfer takes its rows by readlane
+  const int slot = chunk * kSlots + (lane & 31);
+  const int my_idx = slot < nv ? s_idx[slot] : t;
 #pragma unroll
   for (int i = 0; i < kLatDma; ++i) {
-    const int blk = i * kWaves + L.wave;  // wave-uniform 64-unit block
-    const int u = blk * 64 + lane;
-    const int r = u >> 6;
-    const int piece = (u & 48) | ((u & 15) ^ lat_key(r));
-    const int slot = chunk * kSlots + r;
-    const int idx = slot < nv ? s_idx[slot] : t;
-    u32x4* dst = buf + __builtin_amdgcn_readfirstlane(blk * 64);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(lat, (lds_void*)dst, 16, (uint32_t)idx * lat_stb + (uint32_t)piece * 16u,
-                                             0, 0, 0);
+    const int r = i * kWaves + L.wave;  // wave-uniform: a 64-unit block is one latent row
+    const uint32_t idx = (uint32_t)__builtin_amdgcn_readlane(my_idx, r);
+    u32x4* dst = buf + __builtin_amdgcn_readfirstlane(r * 64);
+    // physical unit `lane` of row r holds logical unit (lane & 48) | ((lane & 15) ^ key) = lane ^ key
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(lat, (lds_void*)dst, 16, (uint32_t)((lane ^ lat_key(r)) * 16),
+                                             idx * lat_stb, 0, 0);
   }
 #pragma unroll
   for (int i = 0; i < kRopeDma; ++i) {
-    const int blk = i * kWaves + L.wave;  // wave-uniform 64-dword block of the rotary region
-    const int dw = blk * 64 + lane;       // dword index in the rotary region
-    const int r = dw >> 5;
-    const int unit = ((dw >> 2) & 7) ^ rope_key(r);
-    const int slot = chunk * kSlots + r;
-    const int idx = slot < nv ? s_idx[slot] : t;
+    const int blk = i * kWaves + L.wave;  // wave-uniform 64-dword block: rows 2 blk and 2 blk + 1
+    const uint32_t i0 = (uint32_t)__builtin_amdgcn_readlane(my_idx, 2 * blk);
+    const uint32_t i1 = (uint32_t)__builtin_amdgcn_readlane(my_idx, 2 * blk + 1);
+    const uint32_t idx = lane < 32 ? i0 : i1;
+    const int unit = ((lane >> 2) & 7) ^ rope_key(2 * blk);  // equal for both rows
     uint32_t* dst = (uint32_t*)(buf + kLatRegion) + __builtin_amdgcn_readfirstlane(blk * 64);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(kpe, (lds_void*)dst, 4,
-                                             (uint32_t)idx * kpe_stb + (uint32_t)unit * 16u + (uint32_t)(dw & 3) * 4u, 0, 0,
-                                             0);
+                                             idx * kpe_stb + (uint32_t)(unit * 16 + (lane & 3) * 4), 0, 0, 0);
   }
 }
 
@@ -160,13 +158,23 @@ __device__ __forceinline__ f32x16 qk_partial(const u32x4* buf, const bf16x8* qf,
   for (int j = 0; j < 4; ++j) off[j] = (4 * j + 2 * L.half + L.h2) ^ lk;
   const int lat_row = L.n * kLatUnits;
   const int rope_row = kLatRegion + L.n * kRopeUnits;
-#pragma unroll
-  for (int s = 0; s < kQFrags; ++s) {
-    // k-step s covers latent units 4s + 2 half + h2 (s < 16), then rotary units 4(s-16) + 2 half + h2
+  // k-step s covers latent units 4s + 2 half + h2 (s < 16), then rotary units 4(s-16) + 2 half + h2;
+  // fragments are read kQAhead MFMAs ahead in a fenced order (the waits count exactly)
+  u32x4 a[kQFrags];
+  auto read = [&](int s) {
     const int unit = s < 16 ? lat_row + 16 * (s >> 2) + off[s & 3]
                             : rope_row + ((4 * (s - 16) + 2 * L.half + L.h2) ^ rk);
-    const u32x4 a = buf[unit];
-    sc = mfma_bf16_32x32x16(__builtin_bit_cast(bf16x8, a), qf[s], sc);
+    a[s] = buf[unit];
+  };
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+#pragma unroll
+  for (int s = 0; s < kQAhead; ++s) read(s);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int s = 0; s < kQFrags; ++s) {
+    sc = mfma_bf16_32x32x16(__builtin_bit_cast(bf16x8, a[s]), qf[s], sc);
+    if (s + kQAhead < kQFrags) read(s + kQAhead);
+    __builtin_amdgcn_sched_barrier(0);
   }
   return sc;
 }
@@ -221,26 +229,38 @@ __device__ __forceinline__ void finish_chunk(const u32x4* buf, f32x16 sc, int n_
   int lowp[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) lowp[e] = (4 * e + 2 * L.dh + xsub) ^ key0;
+  bf16x8 pb[2];
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
     f32x8 pf;
 #pragma unroll
     for (int e = 0; e < 8; ++e) pf[e] = sc[8 * s + e];
-    const bf16x8 pb = cvt_bf16x8(pf);
-    const __bf16* elems = (const __bf16*)buf;
+    pb[s] = cvt_bf16x8(pf);
+  }
+  // 16 MFMAs (k-step s = i / 8, output block d = i % 8), fragments read kPvAhead ahead
+  const __bf16* elems = (const __bf16*)buf;
+  bf16x8 vf[2 * kDBlocks];
+  auto read = [&](int i) {
+    const int s = i / kDBlocks, d = i % kDBlocks;
     const int off0 = ((r0 + 16 * s) * kLatUnits + 32 * L.half) * 8 + half_el;
+    const int unit = 16 * (d >> 2) + lowp[d & 3];
+    // one integer index per read keeps the pointer a single GEP from the LDS buffer, so the
+    // read keeps the buffer's alias scope (no wait on gathers into the other buffers)
+    const int i_lo = off0 + unit * 8;
+    const int i_hi = off0 + 8 * kLatUnits * 8 + (unit ^ 2) * 8;
+    const bf16x4 lo4 = lds_read_tr4(&elems[i_lo]);
+    const bf16x4 hi4 = lds_read_tr4(&elems[i_hi]);
+    vf[i] = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
 #pragma unroll
-    for (int d = 0; d < kDBlocks; ++d) {
-      const int unit = 16 * (d >> 2) + lowp[d & 3];
-      // one integer index per read keeps the pointer a single GEP from the LDS buffer, so the
-      // read keeps the buffer's alias scope (no wait on gathers into the other buffers)
-      const int i_lo = off0 + unit * 8;
-      const int i_hi = off0 + 8 * kLatUnits * 8 + (unit ^ 2) * 8;
-      asm volatile("" ::"v"(i_hi));
-      const bf16x4 lo4 = lds_read_tr4(&elems[i_lo]);
-      const bf16x4 hi4 = lds_read_tr4(&elems[i_hi]);
-      o[d] = mfma_bf16_32x32x16(__builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7), pb, o[d]);
-    }
+  for (int i = 0; i < kPvAhead; ++i) read(i);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < 2 * kDBlocks; ++i) {
+    o[i % kDBlocks] = mfma_bf16_32x32x16(vf[i], pb[i / kDBlocks], o[i % kDBlocks]);
+    if (i + kPvAhead < 2 * kDBlocks) read(i + kPvAhead);
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
