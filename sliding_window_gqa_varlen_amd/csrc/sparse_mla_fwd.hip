@@ -47,6 +47,7 @@ constexpr int kLatDma = kLatRegion / 64 / kWaves;   // 4 x 16-byte gathers per l
 constexpr int kRopeDma = kSlots * kRopeUnits * 4 / 64 / kWaves;  // 2 x 4-byte gathers per lane
 constexpr int kDmaPerWave = kLatDma + kRopeDma;     // 6, identical on every wave
 constexpr int kSeg = 2048;                          // index slots compacted at a time
+constexpr int kTokenRun = 64;                       // consecutive tokens per XCD turn
 constexpr int kSlotsPerThread = kSeg / kThreads;    // 4
 constexpr int kQFrags = 18;                         // k-steps of 16 coordinates per wave
 constexpr int kDBlocks = 8;                         // 256 output coordinates per wave / 32
@@ -272,9 +273,11 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_fwd_kernel(SparseMlaPa
   __shared__ u32x4 buf1[kChunkUnits];
   __shared__ u32x4 buf2[kChunkUnits];
 
-  // tokens dealt to XCDs in contiguous ranges (rows of one document share an L2)
-  const int per_xcd = gridDim.x / 8;
-  const int t = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  // tokens dealt to the 8 XCDs in runs of kTokenRun, round-robin: neighbouring tokens (which
+  // name mostly the same rows) share an L2, and every XCD gets an even share of each
+  // document, so the cheap tokens at document starts do not leave whole XCDs idle at the end
+  const int j = blockIdx.x / 8;  // blocks reach an XCD in this order
+  const int t = ((j / kTokenRun) * 8 + blockIdx.x % 8) * kTokenRun + j % kTokenRun;
   if (t >= p.T) return;
 
   Lane L;
@@ -405,7 +408,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_fwd_kernel(SparseMlaPa
 
 hipError_t sparse_mla_fwd_launch(const SparseMlaParams& p, hipStream_t stream) {
   if (p.T <= 0) return hipSuccess;
-  const unsigned gx = (unsigned)((p.T + 7) / 8 * 8);
+  const unsigned gx = (unsigned)((p.T + 8 * kTokenRun - 1) / (8 * kTokenRun) * (8 * kTokenRun));
   const unsigned gy = (unsigned)((p.H + kHeadsPerBlock - 1) / kHeadsPerBlock);
   hipLaunchKernelGGL(sparse_mla_fwd_kernel, dim3(gx, gy), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
