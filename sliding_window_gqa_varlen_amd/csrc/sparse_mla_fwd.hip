@@ -167,6 +167,7 @@ __device__ __forceinline__ f32x16 qk_partial(const u32x4* buf, const bf16x8* qf,
                             : rope_row + ((4 * (s - 16) + 2 * L.half + L.h2) ^ rk);
     a[s] = buf[unit];
   };
+  __builtin_amdgcn_s_setprio(1);  // the wave in its MFMA stream goes first
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
 #pragma unroll
   for (int s = 0; s < kQAhead; ++s) read(s);
@@ -177,6 +178,7 @@ __device__ __forceinline__ f32x16 qk_partial(const u32x4* buf, const bf16x8* qf,
     if (s + kQAhead < kQFrags) read(s + kQAhead);
     __builtin_amdgcn_sched_barrier(0);
   }
+  __builtin_amdgcn_s_setprio(0);
   return sc;
 }
 
@@ -253,6 +255,7 @@ __device__ __forceinline__ void finish_chunk(const u32x4* buf, f32x16 sc, int n_
     const bf16x4 hi4 = lds_read_tr4(&elems[i_hi]);
     vf[i] = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
   };
+  __builtin_amdgcn_s_setprio(1);
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
 #pragma unroll
   for (int i = 0; i < kPvAhead; ++i) read(i);
@@ -263,6 +266,7 @@ __device__ __forceinline__ void finish_chunk(const u32x4* buf, f32x16 sc, int n_
     if (i + kPvAhead < 2 * kDBlocks) read(i + kPvAhead);
     __builtin_amdgcn_sched_barrier(0);
   }
+  __builtin_amdgcn_s_setprio(0);
 }
 
 __global__ __launch_bounds__(kThreads, 1) void sparse_mla_fwd_kernel(SparseMlaParams p) {
