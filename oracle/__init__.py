@@ -21,7 +21,11 @@ What is here, and what pins each function (the pins live in ``tests/``):
 * ``sparse.sparse_mla_ref`` / ``sparse_mla_ref_rows`` — gathered top-k
   attention over a shared latent + rotary key, value = latent.  Pinned by a
   hand case, and by reduction to the dense oracle when every causal key of
-  the document is selected.
+  the document is selected (with or without the rotary part).
+* ``sparse.mla_value_proj_ref`` / ``sparse_mla_value_ref`` — the per-head value
+  up-projection value_weight[h] @ o[t, h] applied after sparse MLA.  Pinned by
+  identity and zero-head weights (exact copies / zeros), and by a scalar triple
+  loop on tiny shapes.
 
 Every function is written in float64 with numpy matmul as its only library
 primitive; there is no blocking or reordering beyond the per-document /
@@ -29,4 +33,5 @@ per-query-block loop that the definition allows.
 """
 from .dense import varlen_attn_ref, varlen_attn_ref_rows  # noqa: F401
 from .mask import allowed_matrix, varlen_attn_bruteforce  # noqa: F401
-from .sparse import sparse_mla_ref, sparse_mla_ref_rows, slot_validity  # noqa: F401
+from .sparse import (mla_value_proj_ref, slot_validity, sparse_mla_ref, sparse_mla_ref_rows,  # noqa: F401
+                     sparse_mla_value_ref)

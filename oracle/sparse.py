@@ -75,3 +75,28 @@ def sparse_mla_ref_rows(q, latent, k_pe, indices, doc_ids, scale: float, tokens)
         outs.append(o)
         lses.append(l)
     return np.stack(outs), np.stack(lses)
+
+
+def mla_value_proj_ref(o_latent, value_weight):
+    """fp64 out_v [T, H, d_v] with out_v[t, h] = value_weight[h] @ o_latent[t, h].
+
+    The KV-B value up-projection that ``sparse_mla`` on the mistral_large4
+    attention page applies to the attention output over latent rows: its
+    value_weight is [heads, value_dim, 512] and it returns [tokens, heads,
+    value_dim].  Empty query rows (o_latent = 0) stay zero.
+    """
+    o = np.asarray(o_latent, dtype=np.float64)
+    w = np.asarray(value_weight, dtype=np.float64)
+    T, H, d_l = o.shape
+    assert w.shape[0] == H and w.shape[2] == d_l
+    out = np.empty((T, H, w.shape[1]))
+    for h in range(H):
+        out[:, h, :] = o[:, h, :] @ w[h].T
+    return out
+
+
+def sparse_mla_value_ref(q, latent, k_pe, indices, doc_ids, value_weight, scale: float):
+    """``sparse_mla`` as the page states it: attention over gathered latent rows, then the
+    value up-projection.  Returns out_v [T, H, d_v] and lse [T, H]."""
+    o, lse = sparse_mla_ref(q, latent, k_pe, indices, doc_ids, scale)
+    return mla_value_proj_ref(o, value_weight), lse

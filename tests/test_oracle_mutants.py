@@ -122,6 +122,39 @@ def sparse_pins_hold(mod) -> bool:
         return False
 
 
+def value_pins_hold(mod) -> bool:
+    """Scalar-loop and identity-weight pins of the value up-projection, plus its composition."""
+    try:
+        rng = np.random.default_rng(31)
+        T, H, dl, dv = 3, 3, 5, 4
+        o = rng.standard_normal((T, H, dl))
+        w = rng.standard_normal((H, dv, dl))
+        got = mod.mla_value_proj_ref(o, w)
+        want = np.zeros((T, H, dv))
+        for t in range(T):
+            for h in range(H):
+                for v in range(dv):
+                    want[t, h, v] = sum(w[h, v, d] * o[t, h, d] for d in range(dl))
+        if not _close(got, want):
+            return False
+        eye = np.zeros((H, dv, dl))
+        eye[:, :, :dv] = np.eye(dv)
+        if not _close(mod.mla_value_proj_ref(o, eye), o[..., :dv], 0.0):
+            return False
+        lengths = [4, 3]
+        q = rng.standard_normal((7, H, dl + 2))
+        lat = rng.standard_normal((7, dl))
+        kpe = rng.standard_normal((7, 2))
+        ids = np.repeat([0, 1], lengths)
+        idx = np.array([[0, -1, -1, -1], [0, 1, -1, -1], [0, 1, 2, -1], [0, 1, 2, 3],
+                        [4, -1, -1, -1], [4, 5, -1, -1], [4, 5, 6, -1]])
+        ov, lv = mod.sparse_mla_value_ref(q, lat, kpe, idx, ids, w, 0.5)
+        oo, ll = oracle.sparse.sparse_mla_ref(q, lat, kpe, idx, ids, 0.5)
+        return _close(ov, np.einsum("hvd,thd->thv", w, oo)) and _close(lv, ll)
+    except Exception:
+        return False
+
+
 DENSE_MUTANTS = [
     ("window off by one", "ok &= (i - j) < window", "ok &= (i - j) <= window"),
     ("window off by one (rows)", "lo = s if window == 0 else max(s, i - window + 1)",
@@ -159,9 +192,23 @@ SPARSE_MUTANTS = [
 ]
 
 
+VALUE_MUTANTS = [
+    ("wrong head's weight", "out[:, h, :] = o[:, h, :] @ w[h].T", "out[:, h, :] = o[:, h, :] @ w[(h + 1) % H].T"),
+    ("latent coordinates reversed", "out[:, h, :] = o[:, h, :] @ w[h].T", "out[:, h, :] = o[:, h, ::-1] @ w[h].T"),
+    ("projection skipped", "return mla_value_proj_ref(o, value_weight), lse",
+     "return o[..., :np.asarray(value_weight).shape[1]], lse"),
+]
+
+
 def test_unmutated_oracle_passes_the_battery():
     assert dense_pins_hold(oracle.dense)
     assert sparse_pins_hold(oracle.sparse)
+    assert value_pins_hold(oracle.sparse)
+
+
+@pytest.mark.parametrize("name,old,new", VALUE_MUTANTS, ids=[m[0] for m in VALUE_MUTANTS])
+def test_value_mutant_is_caught(name, old, new):
+    assert not value_pins_hold(mutated(oracle.sparse, old, new)), f"pins missed mutant: {name}"
 
 
 @pytest.mark.parametrize("name,old,new", DENSE_MUTANTS, ids=[m[0] for m in DENSE_MUTANTS])

@@ -2,7 +2,7 @@
 import numpy as np
 import pytest
 
-from oracle import sparse_mla_ref, sparse_mla_ref_rows, varlen_attn_ref
+from oracle import mla_value_proj_ref, sparse_mla_ref, sparse_mla_ref_rows, sparse_mla_value_ref, varlen_attn_ref
 from tests.golden_util import load
 
 
@@ -122,3 +122,61 @@ def test_padding_query_tokens_are_empty():
     out, lse = sparse_mla_ref(q, latent, k_pe, idx, ids, 1.0)
     assert np.all(out[3:] == 0) and np.all(np.isneginf(lse[3:]))
     assert np.all(np.isfinite(lse[:3]))
+
+
+def test_nope_rows_equal_dense_without_rotary_part():
+    """NoPE layers (k_pe [T, 0], q of width d_l): the all-causal selection is dense MQA on latent."""
+    lengths = [7, 3, 11]
+    H, d_l = 2, 8
+    q, latent, k_pe, ids = rand_sparse(lengths, H, d_l, 0, seed=9)
+    assert k_pe.shape[1] == 0
+    idx = all_causal_indices(lengths, 12)
+    out, lse = sparse_mla_ref(q, latent, k_pe, idx, ids, 0.45)
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    od, ld = varlen_attn_ref(q, latent[:, None, :], latent[:, None, :], cu, 0, 0.45)
+    np.testing.assert_allclose(out, od, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse, ld, rtol=0, atol=1e-13)
+
+
+def test_value_projection_scalar_loop():
+    """out_v[t, h, v] = sum_d value_weight[h, v, d] * o[t, h, d], written as a scalar loop."""
+    rng = np.random.default_rng(21)
+    T, H, d_l, d_v = 3, 2, 5, 4
+    o = rng.standard_normal((T, H, d_l))
+    w = rng.standard_normal((H, d_v, d_l))
+    got = mla_value_proj_ref(o, w)
+    for t in range(T):
+        for h in range(H):
+            for v in range(d_v):
+                acc = 0.0
+                for d in range(d_l):
+                    acc += w[h, v, d] * o[t, h, d]
+                assert got[t, h, v] == pytest.approx(acc, abs=1e-12)
+
+
+def test_value_projection_identity_and_zero_heads():
+    """[I | 0] weights copy the first d_v latent coordinates; a zero head gives zeros."""
+    rng = np.random.default_rng(22)
+    T, H, d_l, d_v = 6, 3, 10, 4
+    o = rng.standard_normal((T, H, d_l))
+    w = np.zeros((H, d_v, d_l))
+    w[0, :, :d_v] = np.eye(d_v)
+    w[2, :, d_l - d_v:] = np.eye(d_v)  # the last d_v coordinates, in order
+    got = mla_value_proj_ref(o, w)
+    np.testing.assert_array_equal(got[:, 0], o[:, 0, :d_v])
+    np.testing.assert_array_equal(got[:, 1], np.zeros((T, d_v)))
+    np.testing.assert_array_equal(got[:, 2], o[:, 2, d_l - d_v:])
+
+
+def test_sparse_mla_value_composes_and_keeps_empty_rows_zero():
+    lengths = [6, 4]
+    H, d_l, d_r, d_v = 3, 6, 2, 5
+    q, latent, k_pe, ids = rand_sparse(lengths, H, d_l, d_r, seed=23)
+    idx = all_causal_indices(lengths, 6)
+    idx[4] = -1  # an empty query row
+    w = np.random.default_rng(24).standard_normal((H, d_v, d_l))
+    out_v, lse = sparse_mla_value_ref(q, latent, k_pe, idx, ids, w, 0.6)
+    o, l = sparse_mla_ref(q, latent, k_pe, idx, ids, 0.6)
+    np.testing.assert_allclose(out_v, np.einsum("hvd,thd->thv", w, o), rtol=0, atol=1e-12)
+    np.testing.assert_array_equal(lse, l)
+    assert np.all(out_v[4] == 0) and np.isneginf(lse[4]).all()
