@@ -22,6 +22,9 @@
  *                   Defined by sparse_mla and MistralLarge4Attention._sparse_forward
  *                   (nemo_automodel.components.models.mistral_large4.attention page).
  *
+ *  mla_value_proj   The per-head value up-projection (value_weight) that sparse_mla
+ *                   applies to sparse_mla_fwd's latent-space output.
+ *
  * Conventions common to every entry point
  *  - Tensors are described by swa_tensor: a device pointer plus shape and strides in
  *    elements. The innermost dimension must be contiguous (stride 1); the other
@@ -140,6 +143,25 @@ int32_t varlen_attn_fwd(const swa_tensor* q, const swa_tensor* k, const swa_tens
 int32_t sparse_mla_fwd(const swa_tensor* q, const swa_tensor* latent, const swa_tensor* k_pe,
                        const swa_tensor* indices, const int32_t* doc_ids, float scale,
                        swa_tensor* out, float* lse, void* stream);
+
+/*
+ * mla_value_proj — value up-projection that follows sparse MLA.
+ *
+ * For every token t and head h:  out[t,h,:] = value_weight[h] @ o_latent[t,h,:]
+ * i.e. out[t,h,v] = sum_d value_weight[h,v,d] * o_latent[t,h,d], accumulated in f32 and
+ * rounded to bf16 once. Defined by sparse_mla (value_weight [heads, value_dim, 512],
+ * returns [tokens, heads, value_dim]) on the
+ * nemo_automodel.components.models.mistral_large4.attention page; applied to the output of
+ * sparse_mla_fwd it completes that operation (rows of zeros stay zero).
+ *
+ *   o_latent      [T, H, 512] bf16 (e.g. sparse_mla_fwd's out)
+ *   value_weight  [H, Dv, 512] bf16
+ *   out           [T, H, Dv] bf16
+ * Supported: Dv in {64, 128}. The grid is sized from the current device's compute-unit
+ * count (queried on the host at each call).
+ */
+int32_t mla_value_proj(const swa_tensor* o_latent, const swa_tensor* value_weight, swa_tensor* out,
+                       void* stream);
 
 /* Static description of a status code. Never NULL. */
 const char* swa_strerror(int32_t status);

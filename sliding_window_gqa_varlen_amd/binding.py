@@ -24,7 +24,8 @@ SWA_DTYPE_F32, SWA_DTYPE_BF16, SWA_DTYPE_I32 = 0, 1, 2
 _DTYPES = {torch.float32: SWA_DTYPE_F32, torch.bfloat16: SWA_DTYPE_BF16, torch.int32: SWA_DTYPE_I32}
 
 # functions the header declares, with their ctypes signatures
-EXPORTS = ("varlen_attn_fwd", "sparse_mla_fwd", "swa_strerror", "swa_last_error", "swa_abi_version")
+EXPORTS = ("varlen_attn_fwd", "sparse_mla_fwd", "mla_value_proj", "swa_strerror", "swa_last_error",
+           "swa_abi_version")
 
 
 class SwaTensor(ctypes.Structure):
@@ -58,6 +59,8 @@ def load_library():
         lib.varlen_attn_fwd.restype = i32
         lib.sparse_mla_fwd.argtypes = [P, P, P, P, vp, f32, P, vp, vp]
         lib.sparse_mla_fwd.restype = i32
+        lib.mla_value_proj.argtypes = [P, P, P, vp]
+        lib.mla_value_proj.restype = i32
         lib.swa_strerror.argtypes = [i32]
         lib.swa_strerror.restype = ctypes.c_char_p
         lib.swa_last_error.argtypes = []
@@ -166,3 +169,33 @@ def sparse_mla_fwd(q: torch.Tensor, latent: torch.Tensor, k_pe: torch.Tensor, in
                             _ptr(doc_ids), float(scale), ctypes.byref(do), _ptr(lse), _stream(stream))
     _check("sparse_mla_fwd", st)
     return out, lse
+
+
+def mla_value_proj(o_latent: torch.Tensor, value_weight: torch.Tensor, out: Optional[torch.Tensor] = None,
+                   stream=None) -> torch.Tensor:
+    """Value up-projection: out[t, h] = value_weight[h] @ o_latent[t, h].
+
+    o_latent [T, H, 512] bf16, value_weight [H, Dv, 512] bf16 (Dv in {64, 128});
+    returns out [T, H, Dv] bf16.
+    """
+    lib = load_library()
+    T, H, _ = o_latent.shape
+    Dv = value_weight.shape[1]
+    if out is None:
+        out = torch.empty((T, H, Dv), dtype=o_latent.dtype, device=o_latent.device)
+    do, dw, dout = describe(o_latent), describe(value_weight), describe(out)
+    st = lib.mla_value_proj(ctypes.byref(do), ctypes.byref(dw), ctypes.byref(dout), _stream(stream))
+    _check("mla_value_proj", st)
+    return out
+
+
+def sparse_mla(q: torch.Tensor, latent: torch.Tensor, k_pe: torch.Tensor, indices: torch.Tensor,
+               doc_ids: torch.Tensor, value_weight: torch.Tensor, scale: Optional[float] = None, stream=None,
+               return_lse: bool = True):
+    """Sparse MLA with the value up-projection: sparse_mla_fwd, then mla_value_proj.
+
+    Returns (out [T, H, Dv] bf16, lse [T, H] fp32 or None).  The latent-space
+    intermediate [T, H, 512] is a torch allocation on the same stream.
+    """
+    o, lse = sparse_mla_fwd(q, latent, k_pe, indices, doc_ids, scale, stream=stream, return_lse=return_lse)
+    return mla_value_proj(o, value_weight, stream=stream), lse

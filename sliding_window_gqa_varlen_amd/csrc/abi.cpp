@@ -211,4 +211,51 @@ int32_t sparse_mla_fwd(const swa_tensor* q, const swa_tensor* latent, const swa_
   return SWA_OK;
 }
 
+int32_t mla_value_proj(const swa_tensor* o_latent, const swa_tensor* value_weight, swa_tensor* out,
+                       void* stream) {
+  g_last_error.clear();
+  int32_t st;
+  if ((st = check_tensor(o_latent, "o_latent", 3)) != SWA_OK) return st;
+  if ((st = check_tensor(value_weight, "value_weight", 3)) != SWA_OK) return st;
+  if ((st = check_tensor(out, "out", 3)) != SWA_OK) return st;
+  if (o_latent->dtype != SWA_DTYPE_BF16 || value_weight->dtype != SWA_DTYPE_BF16 || out->dtype != SWA_DTYPE_BF16)
+    return fail(SWA_ERR_DTYPE, "o_latent, value_weight and out must be bf16");
+  const int64_t T = o_latent->shape[0], H = o_latent->shape[1], Dl = o_latent->shape[2];
+  const int64_t Dv = value_weight->shape[1];
+  if (value_weight->shape[0] != H || value_weight->shape[2] != Dl)
+    return fail(SWA_ERR_SHAPE, "value_weight must be [H, value_dim, latent dim]");
+  if (out->shape[0] != T || out->shape[1] != H || out->shape[2] != Dv)
+    return fail(SWA_ERR_SHAPE, "out must be [T, H, value_dim]");
+  if (Dl != 512) return fail(SWA_ERR_UNSUPPORTED, "only latent dim 512 is supported");
+  if (Dv != 64 && Dv != 128) return fail(SWA_ERR_UNSUPPORTED, "value_dim must be 64 or 128");
+  if (H <= 0 || H > 65535) return fail(SWA_ERR_UNSUPPORTED, "H out of range");
+  if (T > (int64_t)1 << 30) return fail(SWA_ERR_UNSUPPORTED, "T too large");
+  if (value_weight->stride[1] * 2 * Dv > (int64_t)UINT32_MAX)
+    return fail(SWA_ERR_UNSUPPORTED, "value_weight rows too far apart");
+  if (T > 0 && (same_data(out, o_latent) || same_data(out, value_weight)))
+    return fail(SWA_ERR_ARG, "out must not alias an input");
+  if (T == 0) return SWA_OK;
+
+  int dev = 0, n_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n_cu <= 0)
+    return fail(SWA_ERR_LAUNCH, "mla_value_proj: cannot query the device");
+  swa::MlaValueProjParams p{};
+  p.o = o_latent->data;
+  p.w = value_weight->data;
+  p.out = out->data;
+  p.o_st = o_latent->stride[0];
+  p.o_sh = o_latent->stride[1];
+  p.w_sh = value_weight->stride[0];
+  p.w_sv = value_weight->stride[1];
+  p.out_st = out->stride[0];
+  p.out_sh = out->stride[1];
+  p.T = (int32_t)T;
+  p.H = (int32_t)H;
+  p.Dv = (int32_t)Dv;
+  const hipError_t e = swa::mla_value_proj_launch(p, n_cu, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(SWA_ERR_LAUNCH, "mla_value_proj launch: %s", hipGetErrorString(e));
+  return SWA_OK;
+}
+
 }  // extern "C"

@@ -53,4 +53,16 @@ struct SparseMlaParams {
 
 hipError_t sparse_mla_fwd_launch(const SparseMlaParams& p, hipStream_t stream);
 
+// Sparse MLA value up-projection (bf16): out[t, h, :] = w[h] o[t, h, :]. Strides in elements.
+struct MlaValueProjParams {
+  const void* o;  // [T, H, 512]
+  const void* w;  // [H, Dv, 512]
+  void* out;      // [T, H, Dv]
+  int64_t o_st, o_sh, w_sh, w_sv, out_st, out_sh;
+  int32_t T, H, Dv;
+};
+
+// `n_cu`: compute units of the device (sizes the grid for one resident workgroup per CU).
+hipError_t mla_value_proj_launch(const MlaValueProjParams& p, int n_cu, hipStream_t stream);
+
 }  // namespace swa

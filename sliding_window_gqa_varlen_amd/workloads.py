@@ -14,8 +14,10 @@ Recipe (fixed so runs reproduce):
   ``[a, b]``.  Packed document lengths per pack follow the
   ``prepare_magi_inputs`` batch description on the muse_spark magi_cp page.
 * Every tensor then comes from its own stream ``default_rng([seed, stream])``
-  (q=1, k=2, v=3, sinks=4, indices=5, latent=6, k_pe=7), so a tensor can be
-  regenerated without drawing the others.  Values are standard normal float32.
+  (q=1, k=2, v=3, sinks=4, indices=5, latent=6, k_pe=7, value_weight=8), so a
+  tensor can be regenerated without drawing the others.  Values are standard
+  normal float32; the sparse value weight is scaled by 1/sqrt(d_latent) (the
+  usual fan-in initialisation) so its outputs stay of unit order.
 * Configuration "sliding window, RMS-normalised q/k" applies the parameter-free
   RMS normalisation (MuseGlimmerScalelessRMSNorm on the muse_glimmer model
   page, eps 1e-5) over head_dim to q and k before rounding.
@@ -37,7 +39,7 @@ from typing import Optional, Sequence
 
 import numpy as np
 
-STREAM_Q, STREAM_K, STREAM_V, STREAM_SINK, STREAM_IDX, STREAM_LATENT, STREAM_KPE = 1, 2, 3, 4, 5, 6, 7
+STREAM_Q, STREAM_K, STREAM_V, STREAM_SINK, STREAM_IDX, STREAM_LATENT, STREAM_KPE, STREAM_VW = 1, 2, 3, 4, 5, 6, 7, 8
 
 
 # ---------------------------------------------------------------------------
@@ -284,3 +286,9 @@ def make_sparse(w: SparseWorkload, lengths: Optional[Sequence[int]] = None) -> d
     indices = make_sparse_indices(w.seed, lengths, w.T, w.topk)
     return dict(q=q, latent=latent, k_pe=k_pe, indices=indices,
                 doc_ids=doc_ids_from_lengths(w.T, lengths), scale=w.scale, workload=w, lengths=lengths)
+
+
+def make_value_weight(seed: int, H: int, d_value: int, d_latent: int = 512) -> np.ndarray:
+    """value_weight [H, d_value, d_latent] (bf16-exact float32): standard normal / sqrt(d_latent)."""
+    w = normal(seed, STREAM_VW, (H, d_value, d_latent)) * np.float32(1.0 / math.sqrt(d_latent))
+    return round_to_bf16(w)

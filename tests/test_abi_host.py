@@ -175,3 +175,63 @@ def test_sparse_rejects_bad_arguments(lib):
 
 def test_sparse_empty_problem_is_a_no_op(lib):
     assert call_sparse(lib, sparse_args(T=0)) == SWA_OK
+
+
+# ---------------------------------------------------------------- value projection argument checks
+def vproj_args(T=8, H=4, Dv=128, Dl=512):
+    return dict(o=torch.zeros(T, H, Dl, dtype=torch.bfloat16), w=torch.zeros(H, Dv, Dl, dtype=torch.bfloat16),
+                out=torch.zeros(T, H, Dv, dtype=torch.bfloat16))
+
+
+def call_vproj(lib, a, descs=None):
+    d = descs or {n: describe(a[n]) for n in ("o", "w", "out")}
+    ref = lambda x: None if x is None else ctypes.byref(x)  # noqa: E731
+    return lib.mla_value_proj(ref(d["o"]), ref(d["w"]), ref(d["out"]), None)
+
+
+def test_value_proj_rejects_bad_arguments(lib):
+    for name in ("o", "w", "out"):
+        a = vproj_args()
+        d = {n: describe(a[n]) for n in ("o", "w", "out")}
+        d[name] = None
+        assert call_vproj(lib, a, descs=d) == SWA_ERR_NULL
+    a = vproj_args()
+    a["w"] = torch.zeros(4, 128, 512, dtype=torch.float32)
+    assert call_vproj(lib, a) == SWA_ERR_DTYPE
+    a = vproj_args()
+    a["out"] = torch.zeros(8, 4, 128, dtype=torch.float32)
+    assert call_vproj(lib, a) == SWA_ERR_DTYPE
+    a = vproj_args()
+    a["w"] = torch.zeros(5, 128, 512, dtype=torch.bfloat16)
+    assert call_vproj(lib, a) == SWA_ERR_SHAPE
+    a = vproj_args()
+    a["out"] = torch.zeros(8, 4, 64, dtype=torch.bfloat16)
+    assert call_vproj(lib, a) == SWA_ERR_SHAPE
+    a = vproj_args()
+    a["o"] = torch.zeros(8, 2048, dtype=torch.bfloat16)  # rank 2
+    assert call_vproj(lib, a) == SWA_ERR_SHAPE
+    assert call_vproj(lib, vproj_args(Dl=256)) == SWA_ERR_UNSUPPORTED
+    assert call_vproj(lib, vproj_args(Dv=96)) == SWA_ERR_UNSUPPORTED
+    a = vproj_args()
+    a["o"] = a["o"][:, :, :-8]  # innermost extent 504 is checked before any layout question
+    assert call_vproj(lib, a) == SWA_ERR_SHAPE
+    a = vproj_args()
+    a["o"] = torch.zeros(8, 4, 520, dtype=torch.bfloat16)[:, :, 4:516]  # 8-byte misaligned base
+    assert call_vproj(lib, a) == SWA_ERR_LAYOUT
+    a = vproj_args()
+    a["out"] = torch.zeros(8, 4, 256, dtype=torch.bfloat16)[:, :, ::2]  # innermost stride 2
+    assert call_vproj(lib, a) == SWA_ERR_LAYOUT
+
+
+def test_value_proj_rejects_output_aliasing_an_input(lib):
+    a = vproj_args(Dv=128)
+    buf = torch.zeros(8, 4, 512, dtype=torch.bfloat16)
+    a["o"] = buf
+    a["out"] = buf[:, :, :128]
+    assert call_vproj(lib, a) == SWA_ERR_ARG
+
+
+def test_value_proj_empty_problem_is_a_no_op(lib):
+    assert call_vproj(lib, vproj_args(T=0)) == SWA_OK
+    a = vproj_args(T=0)
+    assert binding.mla_value_proj(a["o"], a["w"], stream=0).shape == (0, 4, 128)
