@@ -157,8 +157,10 @@ int32_t sparse_mla_fwd(const swa_tensor* q, const swa_tensor* latent, const swa_
  *   o_latent      [T, H, 512] bf16 (e.g. sparse_mla_fwd's out)
  *   value_weight  [H, Dv, 512] bf16
  *   out           [T, H, Dv] bf16
- * Supported: Dv in {64, 128}. The grid is sized from the current device's compute-unit
- * count (queried on the host at each call).
+ * Supported: Dv in {64, 128}, H <= 65535, and o_latent's token stride below 128 MiB
+ * (SWA_ERR_UNSUPPORTED otherwise). out must not alias an input (SWA_ERR_ARG). T = 0 is a
+ * no-op. The grid is sized from the current device's compute-unit count (queried on the
+ * host at each call).
  */
 int32_t mla_value_proj(const swa_tensor* o_latent, const swa_tensor* value_weight, swa_tensor* out,
                        void* stream);

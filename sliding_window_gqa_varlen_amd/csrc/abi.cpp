@@ -230,8 +230,8 @@ int32_t mla_value_proj(const swa_tensor* o_latent, const swa_tensor* value_weigh
   if (Dv != 64 && Dv != 128) return fail(SWA_ERR_UNSUPPORTED, "value_dim must be 64 or 128");
   if (H <= 0 || H > 65535) return fail(SWA_ERR_UNSUPPORTED, "H out of range");
   if (T > (int64_t)1 << 30) return fail(SWA_ERR_UNSUPPORTED, "T too large");
-  if (value_weight->stride[1] * 2 * Dv > (int64_t)UINT32_MAX)
-    return fail(SWA_ERR_UNSUPPORTED, "value_weight rows too far apart");
+  if (o_latent->stride[0] * 2 * 32 + 1024 > (int64_t)UINT32_MAX)
+    return fail(SWA_ERR_UNSUPPORTED, "o_latent tokens too far apart");
   if (T > 0 && (same_data(out, o_latent) || same_data(out, value_weight)))
     return fail(SWA_ERR_ARG, "out must not alias an input");
   if (T == 0) return SWA_OK;
