@@ -30,11 +30,14 @@ DENSE_SOURCES = ["sliding_window_gqa_varlen_amd/csrc/dense_fwd.hip",
                  "sliding_window_gqa_varlen_amd/csrc/device_common.h"]
 SPARSE_SOURCES = ["sliding_window_gqa_varlen_amd/csrc/sparse_mla_fwd.hip",
                   "sliding_window_gqa_varlen_amd/csrc/device_common.h"]
+VPROJ_SOURCES = ["sliding_window_gqa_varlen_amd/csrc/mla_value_proj.hip",
+                 "sliding_window_gqa_varlen_amd/csrc/device_common.h"]
 TRAFFIC_FILES = {
     "causal_gqa_bf16_t8192": "profiles/dense_fwd_causal_gqa_bf16_t8192_traffic.txt",
     "swa1024_gqa_bf16_t32768": "profiles/dense_fwd_swa1024_gqa_bf16_t32768_traffic.txt",
     "swa128_sink_gqa_bf16_t65536": "profiles/dense_fwd_swa128_sink_gqa_bf16_t65536_traffic.txt",
     "sparse_mla_bf16_t16384": "profiles/sparse_mla_fwd_bf16_t16384_traffic.txt",
+    "mla_value_proj_bf16_t16384": "profiles/mla_value_proj_bf16_t16384_traffic.txt",
 }
 
 
@@ -147,13 +150,30 @@ def cpu_baseline_sparse(inp, budget_s: float = 20.0) -> dict:
             "sample": f"fp64 numpy oracle over {len(done)} random tokens of {T}, {t_total:.1f} s on {cpu_model()}"}
 
 
+def cpu_baseline_vproj(inp, budget_s: float = 15.0) -> dict:
+    import oracle
+    w = inp["workload"]
+    rng = np.random.default_rng(0)
+    done, t_total, nbytes = 0, 0.0, 0
+    while t_total < budget_s:
+        t0 = int(rng.integers(0, w.T - 256 + 1))
+        t = time.perf_counter()
+        oracle.mla_value_proj_ref(inp["o_latent"][t0:t0 + 256], inp["value_weight"])
+        t_total += time.perf_counter() - t
+        done += 256
+        nbytes += metrics.value_proj_bytes(256, w.H, w.d_latent, w.d_value)
+    return {"value": nbytes / t_total / 1e9, "unit": "GB/s", "cores": blas_threads(), "kind": "oracle",
+            "sample": f"fp64 numpy oracle over {done // 256} random runs of 256 tokens of {w.T} (all {w.H} heads), "
+                      f"{t_total:.1f} s on {cpu_model()}"}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="causal_gqa_bf16_t8192",
-                    choices=[w.name for w in W.WORKLOADS])
+                    choices=[w.name for w in W.WORKLOADS + W.VALUE_PROJ_WORKLOADS])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after the timed steps, run a plain device copy of this many MiB (counter calibration)")
@@ -168,10 +188,26 @@ def main() -> int:
 
     binding.load_library()  # raises when the HIP library is missing: there is no fallback path
     dev = torch.device("cuda:0")
-    wl = next(w for w in W.WORKLOADS if w.name == args.workload)
+    wl = next(w for w in W.WORKLOADS + W.VALUE_PROJ_WORKLOADS if w.name == args.workload)
     sparse = isinstance(wl, W.SparseWorkload)
+    vproj = isinstance(wl, W.ValueProjWorkload)
 
-    if sparse:
+    if vproj:
+        inp = W.make_value_proj(wl)
+        o_lat = torch.from_numpy(inp["o_latent"]).to(dev).to(torch.bfloat16)
+        vw = torch.from_numpy(inp["value_weight"]).to(dev).to(torch.bfloat16)
+        out = torch.empty(wl.T, wl.H, wl.d_value, device=dev, dtype=torch.bfloat16)
+
+        def step():
+            binding.mla_value_proj(o_lat, vw, out=out)
+
+        work = metrics.value_proj_bytes(wl.T, wl.H, wl.d_latent, wl.d_value)
+        flops = metrics.value_proj_flops(wl.T, wl.H, wl.d_latent, wl.d_value)
+        sources = VPROJ_SOURCES
+        dtype = "bf16"
+        config = {"workload": wl.name, "tokens": wl.T, "heads": wl.H, "d_latent": wl.d_latent,
+                  "d_value": wl.d_value}
+    elif sparse:
         inp = W.make_sparse(wl)
         q = torch.from_numpy(inp["q"]).to(dev).to(torch.bfloat16)
         lat = torch.from_numpy(inp["latent"]).to(dev).to(torch.bfloat16)
@@ -237,7 +273,12 @@ def main() -> int:
         del a, b
 
     traffic = committed_traffic(wl.name, sources)
-    if sparse:
+    if vproj:
+        achieved = work / (ms * 1e-3) / 1e9
+        value = achieved
+        roof = metrics.roofline("hbm", achieved, metrics.MI355X_HBM_GBPS, "GB/s", traffic)
+        metric, unit = "sparse MLA value up-projection algorithmic HBM GB/s (1 GPU)", "GB/s"
+    elif sparse:
         achieved = work / (ms * 1e-3) / 1e9
         value = achieved
         roof = metrics.roofline("hbm", achieved, metrics.MI355X_HBM_GBPS, "GB/s", traffic)
@@ -258,10 +299,11 @@ def main() -> int:
         "config": config, "roofline": roof,
         "cpu_baseline": None,
     }
-    if sparse:
+    if sparse or vproj:
         line["config"]["tflops"] = flops / (ms * 1e-3) / 1e12
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline_sparse(inp) if sparse else cpu_baseline_dense(inp)
+        line["cpu_baseline"] = (cpu_baseline_vproj(inp) if vproj else
+                                cpu_baseline_sparse(inp) if sparse else cpu_baseline_dense(inp))
     print(json.dumps(line), flush=True)
     return 0
 

@@ -18,6 +18,10 @@
 #include "device_common.h"
 #include "launch.h"
 
+#ifndef SWA_VPROJ_SLOTS128
+#define SWA_VPROJ_SLOTS128 4
+#endif
+
 namespace swa {
 namespace {
 
@@ -26,7 +30,6 @@ constexpr int kWaves = 4;
 constexpr int kDl = 512;                   // latent width (the contraction)
 constexpr int kKSteps = kDl / 16;          // 32 k-steps of 16
 constexpr int kTile = 32;                  // tokens per LDS slot (the MFMA N)
-constexpr int kSlots = 4;                  // ring of 4 x 32 KiB
 constexpr int kRowsPerWave = kTile / kWaves;  // row loads per wave and slot
 constexpr int kSlotBytes = kTile * kDl * 2;
 
@@ -49,6 +52,7 @@ __device__ __forceinline__ void barrier_keep_loads() {
 template <int DV>
 __global__ __launch_bounds__(kThreads, 1) void mla_value_proj_kernel(MlaValueProjParams p) {
   constexpr int MB = DV / 32;           // 32-row blocks of W
+  constexpr int kSlots = DV == 128 ? SWA_VPROJ_SLOTS128 : 4;  // ring of 32 KiB slots
   constexpr int P = kWaves / MB;        // slots consumed per iteration
   constexpr int kAhead = kSlots / P - 1;  // iterations loaded ahead
   constexpr int kIterTokens = kTile * P;

@@ -93,6 +93,15 @@ def sparse_bytes(valid_slots: int, T: int, H: int, d_latent: int, d_rope: int, t
     return gather + q + out + idx + ids + lse
 
 
+def value_proj_bytes(T: int, H: int, d_latent: int, d_value: int) -> int:
+    """Read o_latent and value_weight once, write out once (bf16)."""
+    return 2 * (T * H * d_latent + H * d_value * d_latent + T * H * d_value)
+
+
+def value_proj_flops(T: int, H: int, d_latent: int, d_value: int) -> int:
+    return 2 * T * H * d_latent * d_value
+
+
 def roofline(bound: str, achieved: float, peak: float, unit: str, traffic: Optional[float]) -> dict:
     return {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
             "frac": (achieved / peak) if peak else None, "traffic": traffic}

@@ -116,6 +116,24 @@ WORKLOADS = (
 )
 
 
+
+@dataclasses.dataclass(frozen=True)
+class ValueProjWorkload:
+    """The sparse MLA value up-projection on its own: o_latent [T, H, d_latent] -> [T, H, d_value]."""
+    name: str
+    T: int
+    H: int
+    d_latent: int
+    d_value: int
+    seed: int
+
+
+# The projection at the sparse workload's shape (its attention output feeds this step).
+VALUE_PROJ_WORKLOADS = (
+    ValueProjWorkload("mla_value_proj_bf16_t16384", T=16384, H=128, d_latent=512, d_value=128, seed=4),
+)
+
+
 # ---------------------------------------------------------------------------
 # primitives
 # ---------------------------------------------------------------------------
@@ -292,3 +310,9 @@ def make_value_weight(seed: int, H: int, d_value: int, d_latent: int = 512) -> n
     """value_weight [H, d_value, d_latent] (bf16-exact float32): standard normal / sqrt(d_latent)."""
     w = normal(seed, STREAM_VW, (H, d_value, d_latent)) * np.float32(1.0 / math.sqrt(d_latent))
     return round_to_bf16(w)
+
+
+def make_value_proj(w: ValueProjWorkload) -> dict:
+    """o_latent [T, H, d_latent] standard normal and value_weight [H, d_value, d_latent] (bf16-exact float32)."""
+    o = round_to_bf16(normal(w.seed, STREAM_LATENT, (w.T, w.H, w.d_latent)))
+    return dict(o_latent=o, value_weight=make_value_weight(w.seed, w.H, w.d_value, w.d_latent), workload=w)
