@@ -37,6 +37,7 @@ TRAFFIC_FILES = {
     "swa1024_gqa_bf16_t32768": "profiles/dense_fwd_swa1024_gqa_bf16_t32768_traffic.txt",
     "swa128_sink_gqa_bf16_t65536": "profiles/dense_fwd_swa128_sink_gqa_bf16_t65536_traffic.txt",
     "sparse_mla_bf16_t16384": "profiles/sparse_mla_fwd_bf16_t16384_traffic.txt",
+    "sparse_mla_nope_bf16_t16384": "profiles/sparse_mla_fwd_nope_bf16_t16384_traffic.txt",
     "mla_value_proj_bf16_t16384": "profiles/mla_value_proj_bf16_t16384_traffic.txt",
 }
 
@@ -173,7 +174,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="causal_gqa_bf16_t8192",
-                    choices=[w.name for w in W.WORKLOADS + W.VALUE_PROJ_WORKLOADS])
+                    choices=[w.name for w in W.WORKLOADS + W.EXTRA_WORKLOADS])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after the timed steps, run a plain device copy of this many MiB (counter calibration)")
@@ -188,7 +189,7 @@ def main() -> int:
 
     binding.load_library()  # raises when the HIP library is missing: there is no fallback path
     dev = torch.device("cuda:0")
-    wl = next(w for w in W.WORKLOADS + W.VALUE_PROJ_WORKLOADS if w.name == args.workload)
+    wl = next(w for w in W.WORKLOADS + W.EXTRA_WORKLOADS if w.name == args.workload)
     sparse = isinstance(wl, W.SparseWorkload)
     vproj = isinstance(wl, W.ValueProjWorkload)
 

@@ -138,7 +138,8 @@ int32_t varlen_attn_fwd(const swa_tensor* q, const swa_tensor* k, const swa_tens
  *   scale    finite and > 0
  *   out      [T, H, Dl] bf16
  *   lse      device f32 [T, H] contiguous, or NULL
- * Supported: Dl = 512, Dr = 64, H a multiple of 16.
+ * Supported: Dl = 512, Dr = 64 or Dr = 0 (the NoPE variant: q is [T, H, 512] and k_pe has
+ * no columns; its data pointer may be NULL), H a multiple of 16.
  */
 int32_t sparse_mla_fwd(const swa_tensor* q, const swa_tensor* latent, const swa_tensor* k_pe,
                        const swa_tensor* indices, const int32_t* doc_ids, float scale,

@@ -148,7 +148,8 @@ def sparse_mla_fwd(q: torch.Tensor, latent: torch.Tensor, k_pe: torch.Tensor, in
     """Sparse MLA forward: gathered top-k latent (512) + rotary (64) keys, value = latent.
 
     q [T, H, 576] bf16, latent [T, 512] bf16, k_pe [T, 64] bf16, indices int32
-    [T, topk] (-1 = empty slot), doc_ids int32 [T]; scale defaults to 576 ** -0.5.
+    [T, topk] (-1 = empty slot), doc_ids int32 [T]; scale defaults to q.shape[-1] ** -0.5.
+    NoPE variant: q [T, H, 512] with k_pe [T, 0].
     Returns (out [T, H, 512] bf16, lse [T, H] fp32 or None).
     """
     lib = load_library()

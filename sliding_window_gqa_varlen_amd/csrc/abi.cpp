@@ -171,7 +171,8 @@ int32_t sparse_mla_fwd(const swa_tensor* q, const swa_tensor* latent, const swa_
     return fail(SWA_ERR_SHAPE, "q, latent, k_pe, indices and out must have the same token count");
   if (Dqk != Dl + Dr) return fail(SWA_ERR_SHAPE, "q's last dim must equal latent dim + rotary dim");
   if (out->shape[1] != H || out->shape[2] != Dl) return fail(SWA_ERR_SHAPE, "out must be [T, H, latent dim]");
-  if (Dl != 512 || Dr != 64) return fail(SWA_ERR_UNSUPPORTED, "only latent 512 + rotary 64 is supported");
+  if (Dl != 512 || (Dr != 64 && Dr != 0))
+    return fail(SWA_ERR_UNSUPPORTED, "only latent 512 with rotary 64 or 0 (NoPE) is supported");
   if (H <= 0 || H % 16 != 0 || H > 4096) return fail(SWA_ERR_UNSUPPORTED, "H must be a positive multiple of 16");
   if (topk < 1) return fail(SWA_ERR_ARG, "topk must be >= 1");
   if (topk > (1 << 20)) return fail(SWA_ERR_UNSUPPORTED, "topk too large");
@@ -183,7 +184,7 @@ int32_t sparse_mla_fwd(const swa_tensor* q, const swa_tensor* latent, const swa_
   if (T == 0) return SWA_OK;
   // the gathers address both tensors with 32-bit byte offsets from their bases
   if ((T - 1) * latent->stride[0] * 2 + 1024 > (int64_t)UINT32_MAX ||
-      (T - 1) * k_pe->stride[0] * 2 + 128 > (int64_t)UINT32_MAX)
+      (Dr > 0 && (T - 1) * k_pe->stride[0] * 2 + 128 > (int64_t)UINT32_MAX))
     return fail(SWA_ERR_UNSUPPORTED, "latent or k_pe spans more than 4 GiB");
 
   swa::SparseMlaParams p{};
@@ -197,13 +198,14 @@ int32_t sparse_mla_fwd(const swa_tensor* q, const swa_tensor* latent, const swa_
   p.q_st = q->stride[0];
   p.q_sh = q->stride[1];
   p.lat_st = latent->stride[0];
-  p.kpe_st = k_pe->stride[0];
+  p.kpe_st = Dr > 0 ? k_pe->stride[0] : 0;
   p.idx_st = indices->stride[0];
   p.o_st = out->stride[0];
   p.o_sh = out->stride[1];
   p.T = (int32_t)T;
   p.H = (int32_t)H;
   p.topk = (int32_t)topk;
+  p.Dr = (int32_t)Dr;
   p.scale = scale;
   p.c2 = scale * 1.4426950408889634f;
   const hipError_t e = swa::sparse_mla_fwd_launch(p, reinterpret_cast<hipStream_t>(stream));

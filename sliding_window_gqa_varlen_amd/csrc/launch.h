@@ -38,15 +38,16 @@ hipError_t dense_fwd_launch(const DenseFwdParams& p, Dtype dt, int D, hipStream_
 
 // Sparse MLA forward (bf16). Strides in elements.
 struct SparseMlaParams {
-  const void* q;       // [T, H, 576]
+  const void* q;       // [T, H, 512 + Dr]
   const void* latent;  // [T, 512]
-  const void* k_pe;    // [T, 64]
+  const void* k_pe;    // [T, Dr] (unused when Dr = 0)
   const int32_t* indices;  // [T, topk]
   const int32_t* doc_ids;  // [T]
   void* out;           // [T, H, 512]
   float* lse;          // [T, H] or null
   int64_t q_st, q_sh, lat_st, kpe_st, idx_st, o_st, o_sh;
   int32_t T, H, topk;
+  int32_t Dr;  // rotary width: 64, or 0 (NoPE)
   float scale;
   float c2;
 };

@@ -1,5 +1,7 @@
 // Sparse MLA forward for gfx950: each query token attends to the key rows its top-k index
-// row names; a key is latent[idx] (512) + k_pe[idx] (64) and the value is latent[idx].
+// row names; a key is latent[idx] (512) + k_pe[idx] (64) and the value is latent[idx].  The
+// NoPE variant (no rotary part: q is 512 wide, k_pe has no columns) is the same kernel
+// instantiated with DR = 0.
 // Operation: sparse_mla / MistralLarge4Attention._sparse_forward on the
 // nemo_automodel.components.models.mistral_large4.attention page (-1 = empty slot,
 // empty query rows are zero).
@@ -42,14 +44,16 @@ constexpr int kSlots = 32;                          // slots per chunk
 constexpr int kLatUnits = 64;                       // 16-byte latent units per row
 constexpr int kRopeUnits = 8;                       // 16-byte rotary units per row
 constexpr int kLatRegion = kSlots * kLatUnits;      // 2048 units: latent rows
-constexpr int kChunkUnits = kLatRegion + kSlots * kRopeUnits;  // + 256 units: rotary rows
 constexpr int kLatDma = kLatRegion / 64 / kWaves;   // 4 x 16-byte gathers per lane
 constexpr int kRopeDma = kSlots * kRopeUnits * 4 / 64 / kWaves;  // 2 x 4-byte gathers per lane
-constexpr int kDmaPerWave = kLatDma + kRopeDma;     // 6, identical on every wave
+// per rotary width DR (64, or 0 for the NoPE variant): chunk size in 16-byte units (+ 256
+// units of rotary rows), gathers per wave (identical on every wave), q k-steps per wave
+constexpr int chunk_units(int dr) { return kLatRegion + (dr ? kSlots * kRopeUnits : 0); }
+constexpr int dma_per_wave(int dr) { return kLatDma + (dr ? kRopeDma : 0); }
+constexpr int q_frags(int dr) { return (512 + dr) / 32; }
 constexpr int kSeg = 2048;                          // index slots compacted at a time
 constexpr int kTokenRun = 64;                       // consecutive tokens per XCD turn
 constexpr int kSlotsPerThread = kSeg / kThreads;    // 4
-constexpr int kQFrags = 18;                         // k-steps of 16 coordinates per wave
 constexpr int kDBlocks = 8;                         // 256 output coordinates per wave / 32
 constexpr float kRescaleLog2 = 8.f;                 // lazy-rescale threshold (log2 units)
 constexpr int kQAhead = SWA_SPARSE_QAHEAD;          // QK^T fragments read ahead of their MFMA
@@ -91,6 +95,7 @@ struct Lane {
 // r * 64 + (u & 48) + ((u & 15) ^ lat_key(r)), rotary unit u of row r (as four 4-byte pieces)
 // at 2048 + r * 8 + (u ^ rope_key(r)).
 // Slots past the compacted count (and whole chunks past the end) read the token's own row.
+template <int DR>
 __device__ __forceinline__ void gather_chunk(const SparseMlaParams& p, const int32_t* s_idx, int nv, int chunk,
                                              int t, u32x4* buf, const Lane& L) {
   // MUBUF LDS DMA (buffer_load ... lds): byte offsets from the tensor bases (the host
@@ -98,8 +103,7 @@ __device__ __forceinline__ void gather_chunk(const SparseMlaParams& p, const int
   // transfers leave the LDS read counters exact, so LDS reads below wait only for
   // themselves.
   const __amdgpu_buffer_rsrc_t lat = __builtin_amdgcn_make_buffer_rsrc((void*)p.latent, (short)0, -1, kBufferWord3);
-  const __amdgpu_buffer_rsrc_t kpe = __builtin_amdgcn_make_buffer_rsrc((void*)p.k_pe, (short)0, -1, kBufferWord3);
-  const uint32_t lat_stb = (uint32_t)p.lat_st * 2u, kpe_stb = (uint32_t)p.kpe_st * 2u;
+  const uint32_t lat_stb = (uint32_t)p.lat_st * 2u;
   // recompute the per-lane gather plan here instead of keeping it live across the loop
   int lane = L.lane;
   asm volatile("" : "+v"(lane));
@@ -115,6 +119,9 @@ __device__ __forceinline__ void gather_chunk(const SparseMlaParams& p, const int
     __builtin_amdgcn_raw_ptr_buffer_load_lds(lat, (lds_void*)dst, 16, (uint32_t)((lane ^ lat_key(r)) * 16),
                                              idx * lat_stb, 0, 0);
   }
+  if constexpr (DR == 0) return;
+  const __amdgpu_buffer_rsrc_t kpe = __builtin_amdgcn_make_buffer_rsrc((void*)p.k_pe, (short)0, -1, kBufferWord3);
+  const uint32_t kpe_stb = (uint32_t)p.kpe_st * 2u;
 #pragma unroll
   for (int i = 0; i < kRopeDma; ++i) {
     const int blk = i * kWaves + L.wave;  // wave-uniform 64-dword block: rows 2 blk and 2 blk + 1
@@ -147,9 +154,11 @@ __device__ __forceinline__ Lane opaque_lane(const Lane& Lw) {
   return L;
 }
 
-// Partial S^T[slot][head] over this wave's 18 k-steps of 16 coordinates: global k-step
-// 2 * s + half, i.e. 16-byte units 4 * s + 2 * half + h2 of each gathered row.
+// Partial S^T[slot][head] over this wave's 18 (NoPE: 16) k-steps of 16 coordinates: global
+// k-step 2 * s + half, i.e. 16-byte units 4 * s + 2 * half + h2 of each gathered row.
+template <int DR>
 __device__ __forceinline__ f32x16 qk_partial(const u32x4* buf, const bf16x8* qf, const Lane& Lw) {
+  constexpr int kQFrags = q_frags(DR);
   const Lane L = opaque_lane(Lw);
   f32x16 sc = f32x16{};
   const int lk = lat_key(L.n);
@@ -269,7 +278,11 @@ __device__ __forceinline__ void finish_chunk(const u32x4* buf, f32x16 sc, int n_
   __builtin_amdgcn_s_setprio(0);
 }
 
+template <int DR>
 __global__ __launch_bounds__(kThreads, 1) void sparse_mla_fwd_kernel(SparseMlaParams p) {
+  constexpr int kChunkUnits = chunk_units(DR);
+  constexpr int kDmaPerWave = dma_per_wave(DR);
+  constexpr int kQFrags = q_frags(DR);
   __shared__ int32_t s_idx[kSeg];
   __shared__ int32_t s_wtot[kWaves];
   __shared__ f32x4 exch[kWaves * 4 * 64];
@@ -355,13 +368,13 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_fwd_kernel(SparseMlaPa
     // end), so "own gathers of chunk cc landed" is vmcnt <= kDmaPerWave.
     const int nc = (nv + kSlots - 1) / kSlots;
     if (nc > 0) {  // both prologue gathers unconditionally (chunk 1 may be a dummy)
-      gather_chunk(p, s_idx, nv, 0, t, buf0, L);
-      gather_chunk(p, s_idx, nv, 1, t, buf1, L);
+      gather_chunk<DR>(p, s_idx, nv, 0, t, buf0, L);
+      gather_chunk<DR>(p, s_idx, nv, 1, t, buf1, L);
     }
     auto phase = [&](int cc, const u32x4* cur, u32x4* ahead, bool steady) {
       if (steady) wait_vmcnt<kDmaPerWave>(); else wait_vmcnt<0>();
       barrier_keep_loads();  // chunk cc landed for every wave; chunk cc - 1 fully consumed
-      f32x16 sc = group_ok ? qk_partial(cur, qf, L) : f32x16{};
+      f32x16 sc = group_ok ? qk_partial<DR>(cur, qf, L) : f32x16{};
       const int xl = opaque_lane(L).lane;  // rederived, not kept live across the loop
       f32x4* mine = exch + L.wave * (4 * 64) + xl;
 #pragma unroll
@@ -375,7 +388,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_fwd_kernel(SparseMlaPa
 #pragma unroll
         for (int e = 0; e < 4; ++e) sc[4 * j + e] += v[e];
       }
-      if (steady) gather_chunk(p, s_idx, nv, cc + 2, t, ahead, L);
+      if (steady) gather_chunk<DR>(p, s_idx, nv, cc + 2, t, ahead, L);
       if (group_ok) finish_chunk(cur, sc, min(kSlots, nv - cc * kSlots), o, st, p.c2, L);
     };
     int c = 0;
@@ -414,7 +427,12 @@ hipError_t sparse_mla_fwd_launch(const SparseMlaParams& p, hipStream_t stream) {
   if (p.T <= 0) return hipSuccess;
   const unsigned gx = (unsigned)((p.T + 8 * kTokenRun - 1) / (8 * kTokenRun) * (8 * kTokenRun));
   const unsigned gy = (unsigned)((p.H + kHeadsPerBlock - 1) / kHeadsPerBlock);
-  hipLaunchKernelGGL(sparse_mla_fwd_kernel, dim3(gx, gy), dim3(kThreads), 0, stream, p);
+  if (p.Dr == 64)
+    hipLaunchKernelGGL(sparse_mla_fwd_kernel<64>, dim3(gx, gy), dim3(kThreads), 0, stream, p);
+  else if (p.Dr == 0)
+    hipLaunchKernelGGL(sparse_mla_fwd_kernel<0>, dim3(gx, gy), dim3(kThreads), 0, stream, p);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

@@ -128,8 +128,12 @@ class ValueProjWorkload:
     seed: int
 
 
-# The projection at the sparse workload's shape (its attention output feeds this step).
-VALUE_PROJ_WORKLOADS = (
+# Variants measured beside the five: the sparse workload without the rotary part (NoPE, same
+# documents and index rows), and the value projection at the sparse workload's shape (its
+# attention output feeds that step).
+EXTRA_WORKLOADS = (
+    SparseWorkload("sparse_mla_nope_bf16_t16384", T=16384, H=128, d_latent=512, d_rope=0, topk=2048,
+                   scale=1.0 / math.sqrt(512.0), seed=4, doc_dist=("uniform", 1024, 8192)),
     ValueProjWorkload("mla_value_proj_bf16_t16384", T=16384, H=128, d_latent=512, d_value=128, seed=4),
 )
 

@@ -173,6 +173,19 @@ def test_sparse_rejects_bad_arguments(lib):
     assert call_sparse(lib, a) == SWA_ERR_SHAPE
 
 
+def test_sparse_nope_shapes(lib):
+    """Rotary width 0 (q 512 wide, k_pe [T, 0]) is accepted; other rotary widths are not."""
+    a = sparse_args(T=0)
+    a["q"], a["k_pe"] = torch.zeros(0, 16, 512, dtype=torch.bfloat16), torch.zeros(0, 0, dtype=torch.bfloat16)
+    assert call_sparse(lib, a) == SWA_OK
+    a = sparse_args()
+    a["q"], a["k_pe"] = torch.zeros(8, 16, 544, dtype=torch.bfloat16), torch.zeros(8, 32, dtype=torch.bfloat16)
+    assert call_sparse(lib, a) == SWA_ERR_UNSUPPORTED
+    a = sparse_args()
+    a["k_pe"] = torch.zeros(8, 0, dtype=torch.bfloat16)  # q still 576 wide
+    assert call_sparse(lib, a) == SWA_ERR_SHAPE
+
+
 def test_sparse_empty_problem_is_a_no_op(lib):
     assert call_sparse(lib, sparse_args(T=0)) == SWA_OK
 

@@ -1,4 +1,6 @@
 """GPU parity of sparse_mla_fwd (through the C ABI) against the fp64 oracle."""
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -35,8 +37,8 @@ def oracle(inp, indices=None, doc_ids=None):
                           inp["doc_ids"] if doc_ids is None else doc_ids, inp["scale"])
 
 
-def small(T, topk, seed=4, H=128, lengths=None, dist=("uniform", 64, 600)):
-    w = W.SparseWorkload("sparse_small", T=T, H=H, d_latent=512, d_rope=64, topk=topk, scale=1.0 / 24.0,
+def small(T, topk, seed=4, H=128, lengths=None, dist=("uniform", 64, 600), d_rope=64):
+    w = W.SparseWorkload("sparse_small", T=T, H=H, d_latent=512, d_rope=d_rope, topk=topk, scale=1.0 / 24.0,
                          seed=seed, doc_dist=dist, doc_lengths=None if lengths is None else tuple(lengths))
     return W.make_sparse(w)
 
@@ -170,3 +172,44 @@ def test_repeat_runs_are_bitwise_identical(gpu):
     o1, l1 = run_sparse(inp)
     np.testing.assert_array_equal(o0, o1)
     np.testing.assert_array_equal(l0, l1)
+
+
+# ---------------------------------------------------------------- NoPE variant (no rotary part)
+@pytest.mark.parametrize("T,topk,H", [(300, 64, 128), (1200, 256, 128), (700, 128, 48)])
+def test_nope_small_workloads_elementwise(gpu, T, topk, H):
+    inp = small(T, topk, seed=T + 1, H=H, d_rope=0)
+    assert inp["q"].shape[2] == 512 and inp["k_pe"].shape == (T, 0)
+    ref_o, ref_l = oracle(inp)
+    out, lse = run_sparse(inp)
+    check(out, lse, ref_o, ref_l)
+
+
+def test_nope_all_causal_keys_match_dense_attention(gpu):
+    """NoPE with every causal same-document key selected is dense causal MQA with d_qk = d_v = 512."""
+    lengths = [90, 250, 17]
+    inp = small(357, 256, seed=16, lengths=lengths, d_rope=0)
+    k = inp["latent"][:, None, :]
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    ref_o, ref_l = varlen_attn_ref(inp["q"], k, k, cu, 0, inp["scale"])
+    out, lse = run_sparse(inp)
+    check(out, lse, ref_o, ref_l)
+
+
+def test_nope_full_size_sampled(gpu):
+    """The sparse workload's shape and index rows without the rotary part, on sampled tokens."""
+    import dataclasses
+    w = dataclasses.replace(W.WORKLOADS[4], name="sparse_mla_nope", d_rope=0, scale=1.0 / math.sqrt(512.0))
+    inp = W.make_sparse(w)
+    out, lse = run_sparse(inp)
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
+    T = inp["q"].shape[0]
+    cu = np.concatenate([[0], np.cumsum(inp["lengths"])])
+    rng = np.random.default_rng(2)
+    toks = list(rng.integers(0, T, 30))
+    for d in range(len(cu) - 1):
+        s, e = int(cu[d]), int(cu[d + 1])
+        toks += [s, s + 31, s + 2048, e - 1]
+    toks = np.array(sorted(set(t for t in toks if 0 <= t < T)))
+    ref_o, ref_l = sparse_mla_ref_rows(inp["q"], inp["latent"], inp["k_pe"], inp["indices"], inp["doc_ids"],
+                                       inp["scale"], toks)
+    check(out[toks], lse[toks], ref_o, ref_l)
