@@ -107,7 +107,8 @@ int32_t varlen_attn_fwd(const swa_tensor* q, const swa_tensor* k, const swa_tens
   if (Hq % Hkv != 0) return fail(SWA_ERR_SHAPE, "Hq (%lld) must be a multiple of Hkv (%lld)",
                                  (long long)Hq, (long long)Hkv);
   if (T > (int64_t)1 << 30 || Hq > 65536) return fail(SWA_ERR_UNSUPPORTED, "T or Hq too large");
-  if (D != 64 && D != 128) return fail(SWA_ERR_UNSUPPORTED, "head_dim %lld not supported (64 or 128)", (long long)D);
+  if (D != 64 && D != 128 && !(D == 256 && q->dtype == SWA_DTYPE_BF16))
+    return fail(SWA_ERR_UNSUPPORTED, "head_dim %lld not supported (64 or 128; 256 for bf16)", (long long)D);
   // per-tile row offsets are computed in 32 bits: 64 rows x token stride must fit
   if (k->stride[0] >= (int64_t)1 << 24 || v->stride[0] >= (int64_t)1 << 24)
     return fail(SWA_ERR_UNSUPPORTED, "k/v token stride must be below 2^24 elements");

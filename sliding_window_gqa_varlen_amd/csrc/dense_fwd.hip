@@ -317,15 +317,15 @@ struct Bf {
 // Physical 16-byte unit (within its row) of logical unit u is u ^ key(row).  K rows are
 // read 16 rows at one unit (MFMA A operand); V rows by ds_read_b64_tr_b16, 4 consecutive
 // rows x 4 consecutive units per half-wave.  With 64 banks of 4 bytes, a 256-byte bank line
-// holds one D=128 row or two D=64 rows.
+// holds one D=128 row, two D=64 rows or half a D=256 row.
 template <int D>
 __device__ __forceinline__ int k_key(int r) {
-  if constexpr (D == 128) return r & 15;
+  if constexpr (D >= 128) return r & 15;
   else return (r >> 1) & 7;
 }
 template <int D>
 __device__ __forceinline__ int v_key(int r) {
-  if constexpr (D == 128) return (r & 3) << 2;
+  if constexpr (D >= 128) return (r & 3) << 2;
   else return ((r >> 1) & 1) << 2;
 }
 
@@ -447,10 +447,11 @@ __device__ __forceinline__ float qk_pv_step(const u32x4* kbuf, const u32x4* vbuf
                                             const f32x16 (&sc)[2], float c2, float mu, f32x16 (&o)[Bf<D>::kDBlocks],
                                             f32x16& lacc, float& sn_max) {
   using B = Bf<D>;
-  constexpr int NQ = 2 * B::kQFrags;  // QK^T MFMAs (16 for D = 128, 8 for D = 64)
+  constexpr int NQ = 2 * B::kQFrags;  // QK^T MFMAs (32 for D = 256, 16 for D = 128, 8 for D = 64)
   constexpr int NP = 4 * B::kDBlocks; // PV MFMAs
   constexpr int EPM = 32 / NQ;        // exponentials per QK^T MFMA slot
-  constexpr int kAhead = (D == 128) ? SWA_KAHEAD128 : SWA_KAHEAD64;
+  constexpr int kAhead = (D >= 128) ? SWA_KAHEAD128 : SWA_KAHEAD64;
+  static_assert(32 % NQ == 0, "the 32 exponentials split evenly over the QK^T slots");
   u32x4 frag[NQ + NP];
   __builtin_amdgcn_s_setprio(1);  // the wave in its MFMA stream goes first
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): nothing older is in flight, later waits count exactly
@@ -492,7 +493,7 @@ __device__ __forceinline__ float qk_pv_step(const u32x4* kbuf, const u32x4* vbuf
     __builtin_amdgcn_sched_barrier(0);
   }
   if constexpr (!B::kMfmaRowSum) asm volatile("" ::"v"(rs));  // the row sum is finished inside the stream
-  constexpr int MPM = 16 / NP;  // max3 steps of the new scores per PV MFMA slot
+  // the 16 max steps (two new scores each) over the NP PV slots: steps [16 i / NP, 16 (i + 1) / NP)
   float mx = -INFINITY;
 #pragma unroll
   for (int i = 0; i < NP; ++i) {
@@ -503,8 +504,8 @@ __device__ __forceinline__ float qk_pv_step(const u32x4* kbuf, const u32x4* vbuf
     }
     if (NQ + i + kAhead < NQ + NP) read(NQ + i + kAhead);
 #pragma unroll
-    for (int e = 0; e < MPM; ++e) {
-      const int x = 2 * (i * MPM + e);
+    for (int e = 16 * i / NP; e < 16 * (i + 1) / NP; ++e) {
+      const int x = 2 * e;
       mx = fmaxf(mx, sn[x >> 4][x & 15]);
       mx = fmaxf(mx, sn[x >> 4][(x & 15) + 1]);
     }
@@ -517,7 +518,8 @@ __device__ __forceinline__ float qk_pv_step(const u32x4* kbuf, const u32x4* vbuf
 }
 
 template <int D>
-__global__ __launch_bounds__(kThreads, D == 64 ? SWA_OCC64 : 2) void dense_fwd_bf16_kernel(DenseFwdParams p) {
+__global__ __launch_bounds__(kThreads, D == 64 ? SWA_OCC64 : D == 128 ? 2 : 1) void dense_fwd_bf16_kernel(
+    DenseFwdParams p) {
   using B = Bf<D>;
   __shared__ u32x4 k0[B::kTileUnits];
   __shared__ u32x4 k1[B::kTileUnits];
@@ -743,6 +745,7 @@ hipError_t dense_fwd_launch(const DenseFwdParams& p, Dtype dt, int D, hipStream_
   if (dt == Dtype::BF16) {
     if (D == 128) return launch_kernel(dense_fwd_bf16_kernel<128>, p, stream);
     if (D == 64) return launch_kernel(dense_fwd_bf16_kernel<64>, p, stream);
+    if (D == 256) return launch_kernel(dense_fwd_bf16_kernel<256>, p, stream);
   } else {
     if (D == 128) return launch_kernel(dense_fwd_f32_kernel<128>, p, stream);
     if (D == 64) return launch_kernel(dense_fwd_f32_kernel<64>, p, stream);

@@ -128,10 +128,13 @@ class ValueProjWorkload:
     seed: int
 
 
-# Variants measured beside the five: the sparse workload without the rotary part (NoPE, same
-# documents and index rows), and the value projection at the sparse workload's shape (its
-# attention output feeds that step).
+# Variants measured beside the five: dense full-causal GQA with head_dim 256 (the packed
+# documents of the 8192-token workload, half its heads), the sparse workload without the
+# rotary part (NoPE, same documents and index rows), and the value projection at the sparse
+# workload's shape (its attention output feeds that step).
 EXTRA_WORKLOADS = (
+    DenseWorkload("causal_gqa_d256_bf16_t8192", "bf16", T=8192, Hq=16, Hkv=4, D=256, window=0,
+                  scale=1.0 / 16.0, seed=1, doc_dist=("uniform", 128, 2048)),
     SparseWorkload("sparse_mla_nope_bf16_t16384", T=16384, H=128, d_latent=512, d_rope=0, topk=2048,
                    scale=1.0 / math.sqrt(512.0), seed=4, doc_dist=("uniform", 1024, 8192)),
     ValueProjWorkload("mla_value_proj_bf16_t16384", T=16384, H=128, d_latent=512, d_value=128, seed=4),

@@ -96,9 +96,11 @@ def test_dense_rejects_bad_ranks_shapes_and_dtypes(lib):
     assert call_dense(lib, b) == SWA_ERR_SHAPE
 
 
-@pytest.mark.parametrize("D", [32, 96, 256])
-def test_dense_rejects_unsupported_head_dim(lib, D):
-    assert call_dense(lib, dense_args(D=D)) == SWA_ERR_UNSUPPORTED
+@pytest.mark.parametrize("D,dtype", [(32, torch.bfloat16), (96, torch.bfloat16), (512, torch.bfloat16),
+                                     (256, torch.float32)])
+def test_dense_rejects_unsupported_head_dim(lib, D, dtype):
+    """head_dim 64 and 128 for both dtypes, 256 for bf16 only."""
+    assert call_dense(lib, dense_args(D=D, dtype=dtype)) == SWA_ERR_UNSUPPORTED
 
 
 @pytest.mark.parametrize("kw,code", [

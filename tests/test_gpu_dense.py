@@ -236,3 +236,32 @@ def test_repeat_runs_are_bitwise_identical(gpu):
     o1, l1 = run_dense(inp, "bf16")
     np.testing.assert_array_equal(o0, o1)
     np.testing.assert_array_equal(l0, l1)
+
+
+# ------------------------------------------------------------------ head_dim 256 (bf16)
+def test_head_dim_256_ragged_causal(gpu):
+    lengths = [1, 31, 33, 63, 65, 127, 129, 2, 200]
+    inp = custom(lengths, T=sum(lengths) + 37, Hq=8, Hkv=2, D=256, window=0, dtype="bf16", seed=256)
+    ref_o, ref_l = oracle_full(inp)
+    out, lse = run_dense(inp, "bf16")
+    assert_dense_parity("bf16", out, lse, ref_o, ref_l)
+
+
+@pytest.mark.parametrize("window,sinks", [(65, True), (1, False), (300, True)])
+def test_head_dim_256_windows_sinks_gqa(gpu, window, sinks):
+    lengths = [300, 5, 129, 64]
+    inp = custom(lengths, T=sum(lengths), Hq=16, Hkv=2, D=256, window=window, dtype="bf16", sinks=sinks,
+                 seed=window + 1)
+    ref_o, ref_l = oracle_full(inp)
+    out, lse = run_dense(inp, "bf16")
+    assert_dense_parity("bf16", out, lse, ref_o, ref_l)
+
+
+def test_head_dim_256_packed_documents_elementwise(gpu):
+    """2048 tokens in eight documents of 128..512 tokens, 16 query / 4 KV heads, full causal."""
+    w = W.DenseWorkload("d256", "bf16", T=2048, Hq=16, Hkv=4, D=256, window=0, scale=1.0 / 16.0, seed=7,
+                        doc_dist=("uniform", 128, 512))
+    inp = W.make_dense(w)
+    ref_o, ref_l = oracle_full(inp)
+    out, lse = run_dense(inp, "bf16")
+    assert_dense_parity("bf16", out, lse, ref_o, ref_l)
