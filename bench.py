@@ -26,7 +26,7 @@ sys.path.insert(0, ROOT)
 
 from sliding_window_gqa_varlen_amd import metrics, workloads as W  # noqa: E402
 
-DENSE_SOURCES = ["sliding_window_gqa_varlen_amd/csrc/dense_fwd.hip",
+DENSE_SOURCES = ["sliding_window_gqa_varlen_amd/csrc/dense_fwd.hip", "sliding_window_gqa_varlen_amd/csrc/dense_common.h",
                  "sliding_window_gqa_varlen_amd/csrc/device_common.h"]
 SPARSE_SOURCES = ["sliding_window_gqa_varlen_amd/csrc/sparse_mla_fwd.hip",
                   "sliding_window_gqa_varlen_amd/csrc/device_common.h"]

@@ -1,8 +1,8 @@
 /*
- * swattn.h — C ABI of libswattn.so: forward attention over packed variable-length
- * (THD) token streams on MI355X (gfx950).
+ * swattn.h — C ABI of libswattn.so: attention over packed variable-length (THD)
+ * token streams on MI355X (gfx950).
  *
- * Two operations:
+ * Operations:
  *
  *  varlen_attn_fwd  Causal or causal sliding-window GQA attention over documents
  *                   packed back to back and delimited by cu_seqlens, with a score
@@ -15,6 +15,10 @@
  *                   (nemo_automodel.components.models.muse_glimmer.model page) and
  *                   the causal document mask of SequenceLayout.allowed
  *                   (nemo_automodel.components.models.mistral_large4.attention page).
+ *
+ *  varlen_attn_bwd  Its backward: dq, dk, dv (and dsink) of a loss through out, from
+ *                   the forward's output and log-sum-exp (the pages keep the LSE for
+ *                   the backward and call the attention differentiable).
  *
  *  sparse_mla_fwd   Sparse MLA forward: each query token attends to the top-k key
  *                   rows its index row names; a key is a shared 512-wide latent row
@@ -111,13 +115,48 @@ typedef struct swa_tensor {
  *   out        [T, Hq, D]  same dtype as q
  *   lse        device f32 [T, Hq] contiguous (natural log), or NULL
  *   stream     hipStream_t
- * Supported: D in {64, 128}. Arithmetic: f32 accumulation; bf16 inputs use bf16
+ * Supported: D in {64, 128}, and 256 for bf16. Arithmetic: f32 accumulation; bf16 inputs use bf16
  * matrix products with the probabilities rounded to bf16 for the value product,
  * and the output is rounded once from f32.
  */
 int32_t varlen_attn_fwd(const swa_tensor* q, const swa_tensor* k, const swa_tensor* v,
                         const int32_t* cu_seqlens, int32_t n_docs, int32_t window, float scale,
                         const float* sinks, swa_tensor* out, float* lse, void* stream);
+
+/*
+ * varlen_attn_bwd — backward of varlen_attn_fwd.
+ *
+ * With the forward's definitions (same q, k, v, cu_seqlens, n_docs, window, scale,
+ * sinks), its output out and log-sum-exp lse, and dout = dL/dout, for every allowed
+ * pair (i, j) of a document and query head h (KV head g):
+ *     P_ij   = exp(scale <q[i,h,:], k[j,g,:]> - lse[i,h])
+ *     delta  = <dout[i,h,:], out[i,h,:]>                        (written to delta[i,h])
+ *     dS_ij  = P_ij (<dout[i,h,:], v[j,g,:]> - delta[i,h])
+ *     dq[i,h,:] = scale sum_j dS_ij k[j,g,:]
+ *     dk[j,g,:] = scale sum_{i, h of group g} dS_ij q[i,h,:]
+ *     dv[j,g,:] = sum_{i, h of group g} P_ij dout[i,h,:]
+ *     dsinks[h] = - sum_i exp(sinks[h] - lse[i,h]) delta[i,h]   (with sinks only)
+ * These are the gradients of L through out (lse is treated as auxiliary). Padding
+ * tokens get zero dq, dk and dv and add nothing to dsinks (their lse is -inf).
+ *
+ *   q, out, dout, dq   [T, Hq, D]   bf16
+ *   k, v, dk, dv       [T, Hkv, D]  bf16
+ *   lse                device f32 [T, Hq] contiguous, as written by varlen_attn_fwd
+ *   cu_seqlens, n_docs, window, scale, sinks  as for varlen_attn_fwd
+ *   dsinks             device f32 [Hq], required when sinks is given (written), else
+ *                      ignored
+ *   delta              device f32 [T, Hq] contiguous, written (a workspace the caller
+ *                      owns: the library allocates nothing)
+ *   stream             hipStream_t; four kernels are enqueued in order
+ * Supported: D = 128, T * Hq < 2^30. Errors: as varlen_attn_fwd; SWA_ERR_NULL when lse,
+ * delta or (with sinks) dsinks is NULL; SWA_ERR_ARG when a gradient aliases an input or
+ * another gradient. Arithmetic: bf16 matrix products (P and dS rounded to bf16 as
+ * operands), f32 accumulation, one rounding of each gradient.
+ */
+int32_t varlen_attn_bwd(const swa_tensor* q, const swa_tensor* k, const swa_tensor* v, const swa_tensor* out,
+                        const swa_tensor* dout, const float* lse, const int32_t* cu_seqlens, int32_t n_docs,
+                        int32_t window, float scale, const float* sinks, swa_tensor* dq, swa_tensor* dk,
+                        swa_tensor* dv, float* dsinks, float* delta, void* stream);
 
 /*
  * sparse_mla_fwd — sparse MLA forward over gathered top-k latent rows.

@@ -5,7 +5,7 @@ The compute lives in the HIP library ``libswattn.so`` built from ``csrc/``;
 does not load the library: the first call does, and it raises if the library
 was not built (there is no fallback path).
 """
-__all__ = ["varlen_attn_fwd", "sparse_mla_fwd", "mla_value_proj", "sparse_mla", "library_path"]
+__all__ = ["varlen_attn_fwd", "varlen_attn_bwd", "sparse_mla_fwd", "mla_value_proj", "sparse_mla", "library_path"]
 
 
 def __getattr__(name):

@@ -24,7 +24,7 @@ SWA_DTYPE_F32, SWA_DTYPE_BF16, SWA_DTYPE_I32 = 0, 1, 2
 _DTYPES = {torch.float32: SWA_DTYPE_F32, torch.bfloat16: SWA_DTYPE_BF16, torch.int32: SWA_DTYPE_I32}
 
 # functions the header declares, with their ctypes signatures
-EXPORTS = ("varlen_attn_fwd", "sparse_mla_fwd", "mla_value_proj", "swa_strerror", "swa_last_error",
+EXPORTS = ("varlen_attn_fwd", "varlen_attn_bwd", "sparse_mla_fwd", "mla_value_proj", "swa_strerror", "swa_last_error",
            "swa_abi_version")
 
 
@@ -57,6 +57,8 @@ def load_library():
         vp, i32, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
         lib.varlen_attn_fwd.argtypes = [P, P, P, vp, i32, i32, f32, vp, P, vp, vp]
         lib.varlen_attn_fwd.restype = i32
+        lib.varlen_attn_bwd.argtypes = [P, P, P, P, P, vp, vp, i32, i32, f32, vp, P, P, P, vp, vp, vp]
+        lib.varlen_attn_bwd.restype = i32
         lib.sparse_mla_fwd.argtypes = [P, P, P, P, vp, f32, P, vp, vp]
         lib.sparse_mla_fwd.restype = i32
         lib.mla_value_proj.argtypes = [P, P, P, vp]
@@ -140,6 +142,46 @@ def varlen_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlen
                              _ptr(lse), _stream(stream))
     _check("varlen_attn_fwd", st)
     return out, lse
+
+
+def varlen_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor, dout: torch.Tensor,
+                    lse: torch.Tensor, cu_seqlens: Optional[torch.Tensor], n_docs: Optional[int] = None,
+                    window: int = 0, scale: Optional[float] = None, sinks: Optional[torch.Tensor] = None,
+                    dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
+                    dv: Optional[torch.Tensor] = None, dsinks: Optional[torch.Tensor] = None,
+                    delta: Optional[torch.Tensor] = None, stream=None):
+    """Backward of varlen_attn_fwd (bf16, head_dim 128) from its out and lse.
+
+    Returns (dq, dk, dv, dsinks) — dsinks is None without sinks.  ``delta`` is a
+    [T, Hq] fp32 workspace (allocated here when not given).
+    """
+    lib = load_library()
+    T, Hq, D = q.shape
+    Hkv = k.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if n_docs is None:
+        n_docs = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty((T, Hkv, D), dtype=q.dtype, device=q.device) if dk is None else dk
+    dv = torch.empty((T, Hkv, D), dtype=q.dtype, device=q.device) if dv is None else dv
+    if sinks is not None and dsinks is None:
+        dsinks = torch.empty(Hq, dtype=torch.float32, device=q.device)
+    if delta is None:
+        delta = torch.empty((T, Hq), dtype=torch.float32, device=q.device)
+    for name, x in (("lse", lse), ("delta", delta)):
+        if x.dtype != torch.float32 or not x.is_contiguous() or tuple(x.shape) != (T, Hq):
+            raise ValueError(f"{name} must be a contiguous float32 [T, Hq] tensor")
+    if cu_seqlens is not None and cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    if sinks is not None and sinks.dtype != torch.float32:
+        raise TypeError("sinks must be float32")
+    ds = [describe(x) for x in (q, k, v, out, dout, dq, dk, dv)]
+    st = lib.varlen_attn_bwd(*(ctypes.byref(d) for d in ds[:5]), _ptr(lse), _ptr(cu_seqlens), int(n_docs),
+                             int(window), float(scale), _ptr(sinks), *(ctypes.byref(d) for d in ds[5:]),
+                             _ptr(dsinks), _ptr(delta), _stream(stream))
+    _check("varlen_attn_bwd", st)
+    return dq, dk, dv, (dsinks if sinks is not None else None)
 
 
 def sparse_mla_fwd(q: torch.Tensor, latent: torch.Tensor, k_pe: torch.Tensor, indices: torch.Tensor,

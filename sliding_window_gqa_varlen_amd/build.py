@@ -18,7 +18,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libswattn.so")
 ARCH = os.environ.get("SWA_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["abi.cpp", "dense_fwd.hip", "sparse_mla_fwd.hip", "mla_value_proj.hip"]
+SOURCES = ["abi.cpp", "dense_fwd.hip", "dense_bwd.hip", "sparse_mla_fwd.hip", "mla_value_proj.hip"]
 
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",

@@ -152,6 +152,100 @@ int32_t varlen_attn_fwd(const swa_tensor* q, const swa_tensor* k, const swa_tens
   return SWA_OK;
 }
 
+int32_t varlen_attn_bwd(const swa_tensor* q, const swa_tensor* k, const swa_tensor* v, const swa_tensor* out,
+                        const swa_tensor* dout, const float* lse, const int32_t* cu_seqlens, int32_t n_docs,
+                        int32_t window, float scale, const float* sinks, swa_tensor* dq, swa_tensor* dk,
+                        swa_tensor* dv, float* dsinks, float* delta, void* stream) {
+  g_last_error.clear();
+  int32_t st;
+  const swa_tensor* ins[] = {q, k, v, out, dout};
+  const char* in_names[] = {"q", "k", "v", "out", "dout"};
+  for (int i = 0; i < 5; ++i)
+    if ((st = check_tensor(ins[i], in_names[i], 3)) != SWA_OK) return st;
+  swa_tensor* outs[] = {dq, dk, dv};
+  const char* out_names[] = {"dq", "dk", "dv"};
+  for (int i = 0; i < 3; ++i)
+    if ((st = check_tensor(outs[i], out_names[i], 3)) != SWA_OK) return st;
+  for (int i = 0; i < 5; ++i)
+    if (ins[i]->dtype != SWA_DTYPE_BF16) return fail(SWA_ERR_DTYPE, "%s must be bf16", in_names[i]);
+  for (int i = 0; i < 3; ++i)
+    if (outs[i]->dtype != SWA_DTYPE_BF16) return fail(SWA_ERR_DTYPE, "%s must be bf16", out_names[i]);
+  const int64_t T = q->shape[0], Hq = q->shape[1], D = q->shape[2];
+  const int64_t Hkv = k->shape[1];
+  for (const swa_tensor* t : {q, out, dout, (const swa_tensor*)dq})
+    if (t->shape[0] != T || t->shape[1] != Hq || t->shape[2] != D)
+      return fail(SWA_ERR_SHAPE, "q, out, dout and dq must all be [T, Hq, D]");
+  for (const swa_tensor* t : {k, v, (const swa_tensor*)dk, (const swa_tensor*)dv})
+    if (t->shape[0] != T || t->shape[1] != Hkv || t->shape[2] != D)
+      return fail(SWA_ERR_SHAPE, "k, v, dk and dv must all be [T, Hkv, D]");
+  if (Hq <= 0 || Hkv <= 0) return fail(SWA_ERR_SHAPE, "head counts must be positive");
+  if (Hq % Hkv != 0) return fail(SWA_ERR_SHAPE, "Hq (%lld) must be a multiple of Hkv (%lld)",
+                                 (long long)Hq, (long long)Hkv);
+  if (D != 128) return fail(SWA_ERR_UNSUPPORTED, "backward head_dim %lld not supported (128)", (long long)D);
+  if (T * Hq >= (int64_t)1 << 30) return fail(SWA_ERR_UNSUPPORTED, "T * Hq too large");
+  for (const swa_tensor* t : {q, k, v, dout})
+    if (t->stride[0] >= (int64_t)1 << 24) return fail(SWA_ERR_UNSUPPORTED, "token strides must be below 2^24 elements");
+  if (n_docs < 0) return fail(SWA_ERR_ARG, "n_docs must be >= 0");
+  if (window < 0) return fail(SWA_ERR_ARG, "window must be >= 0");
+  if (!std::isfinite(scale) || !(scale > 0.f)) return fail(SWA_ERR_ARG, "scale must be finite and > 0");
+  if (n_docs > 0 && cu_seqlens == nullptr) return fail(SWA_ERR_NULL, "cu_seqlens is NULL with n_docs > 0");
+  if (T > 0 && (lse == nullptr || delta == nullptr)) return fail(SWA_ERR_NULL, "lse and delta are required");
+  if (T > 0 && sinks != nullptr && dsinks == nullptr) return fail(SWA_ERR_NULL, "dsinks is required with sinks");
+  if (T > 0) {
+    for (const swa_tensor* o : {(const swa_tensor*)dq, (const swa_tensor*)dk, (const swa_tensor*)dv})
+      for (const swa_tensor* i : ins)
+        if (same_data(o, i)) return fail(SWA_ERR_ARG, "gradients must not alias an input");
+    if (same_data(dq, dk) || same_data(dq, dv) || same_data(dk, dv))
+      return fail(SWA_ERR_ARG, "dq, dk and dv must be distinct");
+  }
+  if (T == 0) return SWA_OK;
+  if (static_cast<int64_t>(n_docs) + 2 + T > INT32_MAX / 2) return fail(SWA_ERR_UNSUPPORTED, "too many documents");
+
+  swa::DenseBwdParams p{};
+  swa::DenseFwdParams& f = p.f;
+  f.q = q->data;
+  f.k = k->data;
+  f.v = v->data;
+  f.out = out->data;
+  f.q_st = q->stride[0];
+  f.q_sh = q->stride[1];
+  f.k_st = k->stride[0];
+  f.k_sh = k->stride[1];
+  f.v_st = v->stride[0];
+  f.v_sh = v->stride[1];
+  f.o_st = out->stride[0];
+  f.o_sh = out->stride[1];
+  f.cu_seqlens = n_docs > 0 ? cu_seqlens : nullptr;
+  f.sinks = sinks;
+  f.lse = const_cast<float*>(lse);
+  f.T = (int32_t)T;
+  f.n_docs = n_docs;
+  f.Hq = (int32_t)Hq;
+  f.Hkv = (int32_t)Hkv;
+  f.window = window;
+  f.scale = scale;
+  p.dout = dout->data;
+  p.do_st = dout->stride[0];
+  p.do_sh = dout->stride[1];
+  p.delta = delta;
+  p.dq = dq->data;
+  p.dq_st = dq->stride[0];
+  p.dq_sh = dq->stride[1];
+  p.dk = dk->data;
+  p.dk_st = dk->stride[0];
+  p.dk_sh = dk->stride[1];
+  p.dv = dv->data;
+  p.dv_st = dv->stride[0];
+  p.dv_sh = dv->stride[1];
+  p.dsinks = sinks != nullptr ? dsinks : nullptr;
+  swa::dense_bwd_plan(p);
+  if ((int64_t)f.Hkv * f.n_chunks * f.n_vtiles > INT32_MAX / 2 || (int64_t)f.Hkv * p.kv_n_vtiles > INT32_MAX / 2)
+    return fail(SWA_ERR_UNSUPPORTED, "problem too large for one launch");
+  const hipError_t e = swa::dense_bwd_launch(p, (int)D, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(SWA_ERR_LAUNCH, "varlen_attn_bwd launch: %s", hipGetErrorString(e));
+  return SWA_OK;
+}
+
 int32_t sparse_mla_fwd(const swa_tensor* q, const swa_tensor* latent, const swa_tensor* k_pe,
                        const swa_tensor* indices, const int32_t* doc_ids, float scale,
                        swa_tensor* out, float* lse, void* stream) {

@@ -39,15 +39,11 @@
 //    register-staged, padded LDS layout (parity path, not tuned).
 #include <type_traits>
 
-#include "device_common.h"
-#include "launch.h"
+#include "dense_common.h"
 
 namespace swa {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kBN = 64;    // keys per tile
-constexpr int kXcds = 8;   // MI355X: workgroups are dealt round-robin to 8 XCDs
 constexpr float kRescaleLog2 = 8.f;  // lazy-rescale threshold (log2 units)
 #ifndef SWA_KAHEAD128
 #define SWA_KAHEAD128 8
@@ -59,69 +55,10 @@ constexpr float kRescaleLog2 = 8.f;  // lazy-rescale threshold (log2 units)
 #define SWA_OCC64 3
 #endif
 
-typedef __attribute__((address_space(3))) void lds_void;
-constexpr int kBufferWord3 = 0x00020000;  // buffer descriptor word 3: 32-bit data format, raw access
 constexpr bf16x8 kOnesBf16x8 = {(__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f,
                                 (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f};
 
 typedef __attribute__((address_space(1))) const void glob_cvoid;
-
-// s_waitcnt vmcnt(0) with expcnt / lgkmcnt unconstrained
-__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8)); }
-// workgroup barrier that does not drain outstanding vector-memory loads
-__device__ __forceinline__ void barrier_keep_loads() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-__device__ __forceinline__ int opaque(int x) {
-  asm volatile("" : "+v"(x));
-  return x;
-}
-
-// Segment boundaries: segment 0 = [0, cu[0]) and segment n+1 = [cu[n], T) are padding,
-// segment s in 1..n is document s-1.  Entries are clamped to [0, T].
-__device__ __forceinline__ int seg_bound(const DenseFwdParams& p, int s) {
-  if (s <= 0) return 0;
-  if (s > p.n_docs + 1 || p.cu_seqlens == nullptr) return s > p.n_docs + 1 ? p.T : 0;
-  int x = p.cu_seqlens[s - 1];
-  return x < 0 ? 0 : (x > p.T ? p.T : x);
-}
-
-// The workgroup's query tile: tokens [t0, t_end) of segment `seg`, heads [h0, h0 + HB).
-struct Tile {
-  int g, h0, HB, t0, t_end, seg_start, seg;
-  bool padding;
-};
-
-// Decodes blockIdx into a tile; returns false for idle blocks.
-__device__ __forceinline__ bool decode_tile(const DenseFwdParams& p, Tile& w) {
-  const int per_xcd = gridDim.x / kXcds;
-  const int L = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;  // XCD-aware remap
-  if (L >= p.n_work) return false;
-  const int VT = p.n_vtiles;
-  const int hc = L / VT;
-  const int v = VT - 1 - (L - hc * VT);  // each document's tiles last-first
-  w.g = hc / p.n_chunks;
-  const int chunk = hc - w.g * p.n_chunks;
-  const int TQ = p.tile_tokens;
-  // segment s holding virtual tile v: A(s) = floor(bound(s) / TQ) + s, A(s) <= v < A(s+1)
-  int lo = 0, hi = p.n_docs + 2;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (seg_bound(p, mid) / TQ + mid <= v) lo = mid; else hi = mid;
-  }
-  w.seg = lo;
-  w.seg_start = seg_bound(p, lo);
-  const int seg_end = seg_bound(p, lo + 1);
-  w.t0 = w.seg_start + (v - (w.seg_start / TQ + lo)) * TQ;
-  if (w.t0 >= seg_end) return false;
-  w.t_end = min(w.t0 + TQ, seg_end);
-  w.HB = 1 << p.hb_shift;
-  w.h0 = w.g * p.G + chunk * w.HB;
-  w.padding = (lo == 0 || lo == p.n_docs + 1);
-  return true;
-}
 
 template <typename T, int D>
 __device__ __forceinline__ void write_padding(const DenseFwdParams& p, const Tile& w) {
@@ -140,59 +77,10 @@ __device__ __forceinline__ void write_padding(const DenseFwdParams& p, const Til
       p.lse[(int64_t)(w.t0 + idx / w.HB) * p.Hq + w.h0 + idx % w.HB] = -INFINITY;
 }
 
-// Per-lane query geometry inside the tile.
-struct Cols {
-  int wave, lane, n, h2, tw0, tw1, tq, hq, k_lo, k_hi, n_tiles, W;
-};
-
-__device__ __forceinline__ Cols make_cols(const DenseFwdParams& p, const Tile& w) {
-  Cols c;
-  c.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  c.lane = threadIdx.x & 63;
-  c.n = c.lane & 31;   // query column of this lane
-  c.h2 = c.lane >> 5;  // half-wave
-  const int TW = 32 >> p.hb_shift;
-  c.tw0 = w.t0 + c.wave * TW;
-  c.tw1 = min(c.tw0 + TW, w.t_end) - 1;  // last valid token of this wave (< tw0 if none)
-  c.tq = c.tw0 + (c.n >> p.hb_shift);
-  c.hq = w.h0 + (c.n & (w.HB - 1));
-  c.W = p.window;
-  c.k_lo = c.W ? max(w.seg_start, w.t0 - c.W + 1) : w.seg_start;
-  c.k_hi = w.t_end;
-  c.n_tiles = (c.k_hi - c.k_lo + kBN - 1) / kBN;
-  return c;
-}
-
-// Does the wave see any key of the tile starting at kb?  Does the tile need masking?
-__device__ __forceinline__ bool tile_active(const Cols& c, int kb) {
-  return (c.tw0 <= c.tw1) && (kb <= c.tw1) && (c.W == 0 || kb + kBN - 1 > c.tw0 - c.W);
-}
-__device__ __forceinline__ bool tile_needs_mask(const Cols& c, int kb) {
-  return (kb + kBN - 1 > c.tw0) || (c.W != 0 && kb <= c.tw1 - c.W);
-}
-
 struct Softmax {
   float mref;  // reference max of the scores in log2 units (scale folded in)
   float l;     // running sum of exp2(s * c2 - mref) over this half-wave's keys
 };
-
-// Masks keys outside [doc start, query] and outside the window (tiles that straddle the
-// diagonal or the window edge only).
-__device__ __forceinline__ void mask_tile(f32x16 (&sc)[2], int kb, const Cols& c) {
-  // allowed keys of this lane's query: kb + off with lo <= off <= lo + range, where
-  // off = 32 blk + 8 (a / 4) + 4 h2 + a % 4; the 4 h2 term is folded into lo so every
-  // comparison is against an immediate: one subtract, one unsigned compare, one select
-  const int tq4 = opaque(c.tq - 4 * c.h2);  // recomputed per use, nothing hoisted out of the loop
-  const int lo = c.W ? tq4 - c.W + 1 - kb : -(1 << 30);
-  const unsigned range = (unsigned)(tq4 - kb - lo);
-#pragma unroll
-  for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-    for (int a = 0; a < 16; ++a) {
-      const int off = 32 * blk + 8 * (a >> 2) + (a & 3);
-      sc[blk][a] = (unsigned)(off - lo) <= range ? sc[blk][a] : -INFINITY;
-    }
-}
 
 // Online-softmax statistics of one tile, from this lane's raw score maximum.  Lazy
 // rescale: the reference max moves only when a score exceeds it by more than 2^8, so

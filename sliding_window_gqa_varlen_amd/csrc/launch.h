@@ -36,6 +36,29 @@ int64_t dense_fwd_grid(const DenseFwdParams& p);
 void dense_fwd_plan(DenseFwdParams& p);
 hipError_t dense_fwd_launch(const DenseFwdParams& p, Dtype dt, int D, hipStream_t stream);
 
+// Packed varlen GQA backward (bf16, head_dim 128). `f` carries the forward's geometry and
+// inputs (q, k, v, out = the forward output, lse = the forward LSE, read only); strides in
+// elements.
+struct DenseBwdParams {
+  DenseFwdParams f;
+  const void* dout;
+  int64_t do_st, do_sh;
+  float* delta;  // [T, Hq] contiguous: <dout, out> per row (written)
+  void* dq;
+  int64_t dq_st, dq_sh;
+  void* dk;
+  int64_t dk_st, dk_sh;
+  void* dv;
+  int64_t dv_st, dv_sh;
+  float* dsinks;        // [Hq] or null (written when f.sinks is set)
+  int32_t kv_n_vtiles;  // virtual 128-key tiles per KV head
+  int32_t kv_n_work;    // Hkv * kv_n_vtiles
+};
+
+// Fills the key-tile plan (and, through dense_fwd_plan, the query-tile plan) of p.
+void dense_bwd_plan(DenseBwdParams& p);
+hipError_t dense_bwd_launch(const DenseBwdParams& p, int D, hipStream_t stream);
+
 // Sparse MLA forward (bf16). Strides in elements.
 struct SparseMlaParams {
   const void* q;       // [T, H, 512 + Dr]

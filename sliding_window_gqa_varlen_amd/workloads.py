@@ -14,7 +14,7 @@ Recipe (fixed so runs reproduce):
   ``[a, b]``.  Packed document lengths per pack follow the
   ``prepare_magi_inputs`` batch description on the muse_spark magi_cp page.
 * Every tensor then comes from its own stream ``default_rng([seed, stream])``
-  (q=1, k=2, v=3, sinks=4, indices=5, latent=6, k_pe=7, value_weight=8), so a
+  (q=1, k=2, v=3, sinks=4, indices=5, latent=6, k_pe=7, value_weight=8, dout=9), so a
   tensor can be regenerated without drawing the others.  Values are standard
   normal float32; the sparse value weight is scaled by 1/sqrt(d_latent) (the
   usual fan-in initialisation) so its outputs stay of unit order.
@@ -39,7 +39,8 @@ from typing import Optional, Sequence
 
 import numpy as np
 
-STREAM_Q, STREAM_K, STREAM_V, STREAM_SINK, STREAM_IDX, STREAM_LATENT, STREAM_KPE, STREAM_VW = 1, 2, 3, 4, 5, 6, 7, 8
+STREAM_Q, STREAM_K, STREAM_V, STREAM_SINK, STREAM_IDX, STREAM_LATENT, STREAM_KPE, STREAM_VW, STREAM_DOUT = \
+    1, 2, 3, 4, 5, 6, 7, 8, 9
 
 
 # ---------------------------------------------------------------------------
@@ -323,3 +324,8 @@ def make_value_proj(w: ValueProjWorkload) -> dict:
     """o_latent [T, H, d_latent] standard normal and value_weight [H, d_value, d_latent] (bf16-exact float32)."""
     o = round_to_bf16(normal(w.seed, STREAM_LATENT, (w.T, w.H, w.d_latent)))
     return dict(o_latent=o, value_weight=make_value_weight(w.seed, w.H, w.d_value, w.d_latent), workload=w)
+
+
+def make_dout(seed: int, shape) -> np.ndarray:
+    """Upstream gradient dL/dout for the backward (bf16-exact float32, standard normal)."""
+    return round_to_bf16(normal(seed, STREAM_DOUT, tuple(shape)))

@@ -1,0 +1,268 @@
+"""GPU parity of varlen_attn_bwd (through the C ABI) against the fp64 backward oracle.
+
+The HIP path receives the oracle forward's output (rounded to bf16) and log-sum-exp (rounded
+to fp32) and the same seeded dout; its dq, dk, dv, dsinks are compared element by element.
+
+Tolerance: |got - ref| <= 2e-2 * max(1, |ref|) + 6 * 2^-9 * rss, where rss is the root sum
+of squares of the terms the element sums (dv[j]: P_ij dout[i]; dk[j]: scale dS_ij q[i];
+dq[i]: scale dS_ij k[j]).  Each gradient element is a sum of many terms of either sign (dk
+and dv over every query that sees the key, times the group's heads); the kernel rounds P and
+dS to bf16 as matrix operands (relative error at most 2^-9, independent per term), so its
+error has a standard deviation below 2^-9 rss, which can exceed 2e-2 where the terms cancel
+to a small result.  The first part is the forward's bf16 bar (one rounding of the result).
+
+dsinks_h = -sum_i p_sink_i delta_i is a sum whose terms cancel (delta_i = <dout_i, out_i> has
+either sign), so a relative bar does not apply.  Its error is set by the bf16 out the kernel
+receives: rounding element e of out moves the sum by p_sink_i dout_ie out_ie times a relative
+error of at most 2^-9, independently per element, so the error has a standard deviation below
+sigma_h = 2^-9 sqrt(sum_{i,e} (p_sink_i dout_ie out_ie)^2).  The bar is 6 sigma_h +
+1e-3 * max(1, |ref|).  A second check recomputes the sum in fp64 from the very bf16 out the
+kernel was given and holds the kernel to 1e-4 of sum_i p_sink_i |delta_i| (fp32 summation).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import varlen_attn_bwd_ref, varlen_attn_ref
+from sliding_window_gqa_varlen_amd import varlen_attn_bwd, varlen_attn_fwd, workloads as W
+from tests.gpu_util import dev
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2
+
+
+def custom(lengths, T, Hq, Hkv, window, sinks=False, seed=0, D=128):
+    w = W.DenseWorkload("custom", "bf16", T=T, Hq=Hq, Hkv=Hkv, D=D, window=window, scale=1.0 / math.sqrt(D),
+                        seed=seed, doc_lengths=tuple(lengths), sinks=sinks)
+    return W.make_dense(w)
+
+
+def dout_for(inp, seed):
+    return W.make_dout(seed, inp["q"].shape)
+
+
+def gpu_forward(inp):
+    q, k, v = (dev(inp[n], torch.bfloat16) for n in ("q", "k", "v"))
+    cu = torch.from_numpy(inp["cu_seqlens"]).cuda()
+    s = None if inp["sinks"] is None else torch.from_numpy(np.asarray(inp["sinks"], np.float32)).cuda()
+    return varlen_attn_fwd(q, k, v, cu, inp["n_docs"], inp["window"], inp["scale"], s)
+
+
+def run_bwd(inp, do, window=None, out=None, lse=None):
+    """HIP backward on the oracle's forward output (or the given out / lse tensors)."""
+    win = inp["window"] if window is None else window
+    if out is None:
+        ref_o, ref_l = varlen_attn_ref(inp["q"], inp["k"], inp["v"], inp["cu_seqlens"], win, inp["scale"],
+                                       inp["sinks"])
+        out = dev(ref_o, torch.bfloat16)
+        lse = torch.from_numpy(ref_l.astype(np.float32)).cuda()
+    q, k, v = (dev(inp[n], torch.bfloat16) for n in ("q", "k", "v"))
+    cu = torch.from_numpy(inp["cu_seqlens"]).cuda()
+    s = None if inp["sinks"] is None else torch.from_numpy(np.asarray(inp["sinks"], np.float32)).cuda()
+    dq, dk, dv, ds = varlen_attn_bwd(q, k, v, out, dev(do, torch.bfloat16), lse, cu, inp["n_docs"], win,
+                                     inp["scale"], s)
+    torch.cuda.synchronize()
+    f = lambda x: None if x is None else x.float().cpu().numpy().astype(np.float64)  # noqa: E731
+    return f(dq), f(dk), f(dv), f(ds)
+
+
+def oracle_bwd(inp, do, window=None):
+    win = inp["window"] if window is None else window
+    return varlen_attn_bwd_ref(inp["q"], inp["k"], inp["v"], do, inp["cu_seqlens"], win, inp["scale"],
+                               inp["sinks"])[:4]
+
+
+def term_rss(q, k, v, do, cu, window, scale, sinks):
+    """Root sum of squares of the terms each dq, dk, dv element sums (tolerance only)."""
+    q, k, v, do = (np.asarray(x, np.float64) for x in (q, k, v, do))
+    T, Hq, D = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    rq, rk, rv = np.zeros(q.shape), np.zeros(k.shape), np.zeros(v.shape)
+    for d in range(len(cu) - 1):
+        s, e = int(cu[d]), int(cu[d + 1])
+        if e <= s:
+            continue
+        i, j = np.arange(s, e)[:, None], np.arange(s, e)[None, :]
+        ok = (j <= i) & ((window == 0) | (i - j < window))
+        for h in range(Hq):
+            g = h // G
+            S = np.where(ok, scale * q[s:e, h] @ k[s:e, g].T, -np.inf)
+            m = S.max(axis=1)
+            if sinks is not None:
+                m = np.maximum(m, sinks[h])
+            E = np.exp(S - m[:, None])
+            Z = E.sum(axis=1) + (0.0 if sinks is None else np.exp(sinks[h] - m))
+            P = E / Z[:, None]
+            dP = do[s:e, h] @ v[s:e, g].T
+            dS = P * (dP - (P * dP).sum(axis=1, keepdims=True))
+            rv[s:e, g] += (P ** 2).T @ do[s:e, h] ** 2
+            rk[s:e, g] += scale ** 2 * (dS ** 2).T @ q[s:e, h] ** 2
+            rq[s:e, h] = scale ** 2 * (dS ** 2) @ k[s:e, g] ** 2
+    return np.sqrt(rq), np.sqrt(rk), np.sqrt(rv)
+
+
+def check(got, ref, what, rss):
+    assert got.shape == ref.shape, what
+    assert np.all(np.isfinite(got)), f"{what}: non-finite values"
+    bar = TOL * np.maximum(1.0, np.abs(ref)) + 6 * 2.0 ** -9 * rss
+    err = np.abs(got - ref) / bar
+    i = np.unravel_index(np.argmax(err), err.shape)
+    assert err.max() <= 1.0, f"{what}: error {err.max():.2f} x its bar at {i} (got {got[i]:.5f}, ref {ref[i]:.5f})"
+
+
+def sink_probabilities(inp, window=None):
+    win = inp["window"] if window is None else window
+    o, l = varlen_attn_ref(inp["q"], inp["k"], inp["v"], inp["cu_seqlens"], win, inp["scale"], inp["sinks"])
+    with np.errstate(over="ignore"):
+        p = np.where(np.isneginf(l), 0.0, np.exp(np.asarray(inp["sinks"], np.float64)[None, :] - l))
+    return o, p
+
+
+def check_all(got, ref, inp=None, do=None, window=None, out_given=None, lse_given=None):
+    win = inp["window"] if window is None else window
+    rss = term_rss(inp["q"], inp["k"], inp["v"], do, inp["cu_seqlens"], win, inp["scale"], inp["sinks"])
+    for name, g, r, x in zip(("dq", "dk", "dv"), got, ref, rss):
+        check(g, r, name, x)
+    if ref[3] is None:
+        assert got[3] is None
+        return
+    g, r = got[3], ref[3]
+    o, p = sink_probabilities(inp, window)
+    d = np.asarray(do, np.float64)
+    sigma = 2.0 ** -9 * np.sqrt(((p[:, :, None] * d * o) ** 2).sum(axis=(0, 2)))
+    err = np.abs(g - r)
+    bar = 6 * sigma + 1e-3 * np.maximum(1.0, np.abs(r))
+    assert np.all(err <= bar), f"dsinks: error {err.max():.3e} beyond its rounding bar {bar[np.argmax(err - bar)]:.3e}"
+    ob = W.round_to_bf16(o.astype(np.float32)).astype(np.float64) if out_given is None else out_given
+    if lse_given is not None:
+        with np.errstate(over="ignore"):
+            p = np.where(np.isneginf(lse_given), 0.0,
+                         np.exp(np.asarray(inp["sinks"], np.float64)[None, :] - lse_given))
+    delta_b = (d * ob).sum(axis=2)
+    same_input = -(p * delta_b).sum(axis=0)
+    assert np.all(np.abs(g - same_input) <= 1e-4 * np.maximum(1.0, (p * np.abs(delta_b)).sum(axis=0)))
+
+
+@pytest.mark.parametrize("sinks", [False, True])
+def test_ragged_documents_and_padding_tail(gpu, sinks):
+    lengths = [1, 31, 33, 63, 65, 127, 129, 2, 200]
+    inp = custom(lengths, T=sum(lengths) + 37, Hq=8, Hkv=2, window=0, sinks=sinks, seed=1 + sinks)
+    do = dout_for(inp, 3)
+    got = run_bwd(inp, do)
+    check_all(got, oracle_bwd(inp, do), inp, do)
+    T0 = sum(lengths)
+    assert np.all(got[0][T0:] == 0) and np.all(got[1][T0:] == 0) and np.all(got[2][T0:] == 0)
+
+
+@pytest.mark.parametrize("window", [1, 17, 64, 65, 100, 200])
+def test_windows_with_sinks(gpu, window):
+    lengths = [300, 5, 129, 64]
+    inp = custom(lengths, T=sum(lengths), Hq=16, Hkv=2, window=window, sinks=True, seed=window)
+    do = dout_for(inp, window)
+    check_all(run_bwd(inp, do), oracle_bwd(inp, do), inp, do)
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(4, 4), (6, 1), (12, 2), (40, 8), (64, 1)])
+def test_gqa_group_shapes(gpu, Hq, Hkv):
+    lengths = [100, 37, 150]
+    inp = custom(lengths, T=287, Hq=Hq, Hkv=Hkv, window=50, sinks=True, seed=Hq + Hkv)
+    do = dout_for(inp, 7)
+    check_all(run_bwd(inp, do), oracle_bwd(inp, do), inp, do)
+
+
+def test_zero_length_documents_head_and_tail_padding(gpu):
+    lengths = [0, 40, 0, 0, 70, 1, 0]
+    inp = custom(lengths, T=130, Hq=8, Hkv=2, window=0, sinks=True, seed=5)
+    inp["cu_seqlens"] = inp["cu_seqlens"] + 9  # tokens 0..8 sit before the first document
+    do = dout_for(inp, 5)
+    got = run_bwd(inp, do)
+    check_all(got, oracle_bwd(inp, do), inp, do)
+    for g in got[:3]:
+        assert np.all(g[:9] == 0) and np.all(g[120:] == 0)
+
+
+def test_packed_documents_elementwise(gpu):
+    """2048 tokens in documents of 128..512 tokens, 16 query / 4 KV heads, full causal."""
+    w = W.DenseWorkload("bwd", "bf16", T=2048, Hq=16, Hkv=4, D=128, window=0, scale=1.0 / math.sqrt(128.0),
+                        seed=8, doc_dist=("uniform", 128, 512))
+    inp = W.make_dense(w)
+    do = dout_for(inp, 8)
+    check_all(run_bwd(inp, do), oracle_bwd(inp, do), inp, do)
+
+
+@pytest.mark.parametrize("idx", [1, 2])
+def test_full_size_workloads_on_chosen_documents(gpu, idx):
+    """The full-size workloads in the bench's launch configuration (out and lse from the GPU
+    forward); the oracle recomputes whole documents (documents are independent), the smallest
+    ones plus one of ~1100 tokens."""
+    inp = W.make_dense(W.WORKLOADS[idx])
+    do = dout_for(inp, 10 + idx)
+    out, lse = gpu_forward(inp)
+    got = run_bwd(inp, do, out=out, lse=lse)
+    cu = inp["cu_seqlens"]
+    lens = np.diff(cu)
+    order = list(np.argsort(lens)[:2]) + [int(np.argmin(np.abs(lens - 1100)))]
+    for d in sorted(set(order)):
+        s, e = int(cu[d]), int(cu[d + 1])
+        sl = slice(s, e)
+        args = (inp["q"][sl], inp["k"][sl], inp["v"][sl], do[sl], [0, e - s], inp["window"], inp["scale"],
+                inp["sinks"])
+        ref = varlen_attn_bwd_ref(*args)
+        rss = term_rss(*args)
+        for name, g, r, x in zip(("dq", "dk", "dv"), got[:3], ref[:3], rss):
+            check(g[sl], r, f"{name} of document {d} ({e - s} tokens)", x)
+
+
+def test_with_the_gpu_forward_outputs(gpu):
+    """out and lse straight from varlen_attn_fwd (bf16 out, fp32 lse) feed the backward."""
+    lengths = [120, 300, 80]
+    inp = custom(lengths, T=500, Hq=8, Hkv=2, window=90, sinks=True, seed=31)
+    out, lse = gpu_forward(inp)
+    do = dout_for(inp, 31)
+    ob = out.float().cpu().numpy().astype(np.float64)
+    lb = lse.cpu().numpy().astype(np.float64)
+    check_all(run_bwd(inp, do, out=out, lse=lse), oracle_bwd(inp, do), inp, do, out_given=ob, lse_given=lb)
+
+
+def test_window_at_least_document_length_is_bitwise_full_causal(gpu):
+    lengths = [250, 40, 123]
+    inp = custom(lengths, T=413, Hq=8, Hkv=4, window=0, seed=4)
+    do = dout_for(inp, 4)
+    a = run_bwd(inp, do)
+    b = run_bwd(inp, do, window=250)
+    for x, y in zip(a[:3], b[:3]):
+        np.testing.assert_array_equal(x, y)
+
+
+def test_strided_views_of_fused_buffers(gpu):
+    """q, k, v as views of one [T, Hq + 2 Hkv, D] buffer; dq, dk, dv as views of another."""
+    lengths = [77, 130]
+    inp = custom(lengths, T=207, Hq=8, Hkv=2, window=0, sinks=False, seed=6)
+    do = dout_for(inp, 6)
+    ref_o, ref_l = varlen_attn_ref(inp["q"], inp["k"], inp["v"], inp["cu_seqlens"], 0, inp["scale"], None)
+    qkv = torch.cat([dev(inp[n], torch.bfloat16) for n in ("q", "k", "v")], dim=1)
+    q, k, v = qkv[:, :8], qkv[:, 8:10], qkv[:, 10:12]
+    grads = torch.full((207, 12, 128), 7.0, dtype=torch.bfloat16, device="cuda")
+    dq, dk, dv = grads[:, :8], grads[:, 8:10], grads[:, 10:12]
+    cu = torch.from_numpy(inp["cu_seqlens"]).cuda()
+    lse = torch.from_numpy(ref_l.astype(np.float32)).cuda()
+    varlen_attn_bwd(q, k, v, dev(ref_o, torch.bfloat16), dev(do, torch.bfloat16), lse, cu, 2, 0, inp["scale"],
+                    None, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    ref = oracle_bwd(inp, do)
+    rss = term_rss(inp["q"], inp["k"], inp["v"], do, inp["cu_seqlens"], 0, inp["scale"], None)
+    for name, g, r, x in zip(("dq", "dk", "dv"), (dq, dk, dv), ref[:3], rss):
+        check(g.float().cpu().numpy().astype(np.float64), r, name, x)
+
+
+def test_repeat_runs_are_bitwise_identical(gpu):
+    lengths = [300, 211]
+    inp = custom(lengths, T=511, Hq=16, Hkv=4, window=0, sinks=True, seed=12)
+    do = dout_for(inp, 12)
+    a, b = run_bwd(inp, do), run_bwd(inp, do)
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)
