@@ -30,6 +30,8 @@ DENSE_SOURCES = ["sliding_window_gqa_varlen_amd/csrc/dense_fwd.hip", "sliding_wi
                  "sliding_window_gqa_varlen_amd/csrc/device_common.h"]
 SPARSE_SOURCES = ["sliding_window_gqa_varlen_amd/csrc/sparse_mla_fwd.hip",
                   "sliding_window_gqa_varlen_amd/csrc/device_common.h"]
+BWD_SOURCES = ["sliding_window_gqa_varlen_amd/csrc/dense_bwd.hip", "sliding_window_gqa_varlen_amd/csrc/dense_common.h",
+               "sliding_window_gqa_varlen_amd/csrc/device_common.h"]
 VPROJ_SOURCES = ["sliding_window_gqa_varlen_amd/csrc/mla_value_proj.hip",
                  "sliding_window_gqa_varlen_amd/csrc/device_common.h"]
 TRAFFIC_FILES = {
@@ -37,6 +39,8 @@ TRAFFIC_FILES = {
     "swa1024_gqa_bf16_t32768": "profiles/dense_fwd_swa1024_gqa_bf16_t32768_traffic.txt",
     "swa128_sink_gqa_bf16_t65536": "profiles/dense_fwd_swa128_sink_gqa_bf16_t65536_traffic.txt",
     "causal_gqa_d256_bf16_t8192": "profiles/dense_fwd_causal_gqa_d256_bf16_t8192_traffic.txt",
+    "causal_gqa_bwd_bf16_t8192": "profiles/dense_bwd_causal_gqa_bf16_t8192_traffic.txt",
+    "swa1024_gqa_bwd_bf16_t32768": "profiles/dense_bwd_swa1024_gqa_bf16_t32768_traffic.txt",
     "sparse_mla_bf16_t16384": "profiles/sparse_mla_fwd_bf16_t16384_traffic.txt",
     "sparse_mla_nope_bf16_t16384": "profiles/sparse_mla_fwd_nope_bf16_t16384_traffic.txt",
     "mla_value_proj_bf16_t16384": "profiles/mla_value_proj_bf16_t16384_traffic.txt",
@@ -121,6 +125,33 @@ def cpu_baseline_dense(inp, min_s: float = 10.0, max_s: float = 30.0) -> dict:
     return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": blas_threads(), "kind": "oracle",
             "sample": f"fp64 numpy oracle, {len(done)} document calls ({passes} pass(es) over the {n_docs} "
                       f"documents of the workload, all {w.Hq} heads), {t_total:.1f} s on {cpu_model()}"}
+
+
+def cpu_baseline_dense_bwd(inp, min_s: float = 10.0, max_s: float = 30.0) -> dict:
+    """The fp64 backward oracle as it stands, document by document (as the forward's leg)."""
+    import oracle
+    cu = inp["cu_seqlens"]
+    w = inp["workload"]
+    do = W.make_dout(w.seed, inp["q"].shape)
+    done, t_total, passes = [], 0.0, 0
+    while t_total < min_s:
+        for d in range(len(cu) - 1):
+            s, e = int(cu[d]), int(cu[d + 1])
+            sl = slice(s, e)
+            t = time.perf_counter()
+            oracle.varlen_attn_bwd_ref(inp["q"][sl], inp["k"][sl], inp["v"][sl], do[sl], [0, e - s], inp["window"],
+                                       inp["scale"], inp["sinks"])
+            t_total += time.perf_counter() - t
+            done.append(e - s)
+            if t_total >= max_s:
+                break
+        passes += 1
+        if t_total >= max_s:
+            break
+    flops = metrics.dense_bwd_flops(done, inp["window"], w.Hq, w.D)
+    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": blas_threads(), "kind": "oracle",
+            "sample": f"fp64 numpy backward oracle, {len(done)} document calls ({passes} pass(es) over the "
+                      f"{len(cu) - 1} documents, all {w.Hq} heads), {t_total:.1f} s on {cpu_model()}"}
 
 
 def cpu_baseline_sparse(inp, budget_s: float = 20.0) -> dict:
@@ -209,6 +240,29 @@ def main() -> int:
         dtype = "bf16"
         config = {"workload": wl.name, "tokens": wl.T, "heads": wl.H, "d_latent": wl.d_latent,
                   "d_value": wl.d_value}
+    elif getattr(wl, "backward", False):
+        inp = W.make_dense(wl)
+        q, k, v = (torch.from_numpy(inp[n]).to(dev).to(torch.bfloat16) for n in ("q", "k", "v"))
+        cu = torch.from_numpy(inp["cu_seqlens"]).to(dev)
+        sinks = None if inp["sinks"] is None else torch.from_numpy(inp["sinks"]).to(dev)
+        o_fwd, lse = binding.varlen_attn_fwd(q, k, v, cu, inp["n_docs"], wl.window, wl.scale, sinks)
+        dout = torch.from_numpy(W.make_dout(wl.seed, inp["q"].shape)).to(dev).to(torch.bfloat16)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        delta = torch.empty(wl.T, wl.Hq, device=dev, dtype=torch.float32)
+        dsinks = None if sinks is None else torch.empty(wl.Hq, device=dev, dtype=torch.float32)
+
+        def step():
+            binding.varlen_attn_bwd(q, k, v, o_fwd, dout, lse, cu, inp["n_docs"], wl.window, wl.scale, sinks,
+                                    dq=dq, dk=dk, dv=dv, dsinks=dsinks, delta=delta)
+
+        flops = metrics.dense_bwd_flops(inp["lengths"], wl.window, wl.Hq, wl.D)
+        work = flops
+        sources = BWD_SOURCES
+        dtype = "bf16"
+        config = {"workload": wl.name, "tokens": wl.T, "documents": inp["n_docs"], "q_heads": wl.Hq,
+                  "kv_heads": wl.Hkv, "head_dim": wl.D, "window": wl.window, "sinks": wl.sinks,
+                  "allowed_pairs": metrics.dense_allowed_pairs(inp["lengths"], wl.window),
+                  "kernels": "delta, dq, dk/dv (one varlen_attn_bwd call)"}
     elif sparse:
         inp = W.make_sparse(wl)
         q = torch.from_numpy(inp["q"]).to(dev).to(torch.bfloat16)
@@ -280,6 +334,12 @@ def main() -> int:
         value = achieved
         roof = metrics.roofline("hbm", achieved, metrics.MI355X_HBM_GBPS, "GB/s", traffic)
         metric, unit = "sparse MLA value up-projection algorithmic HBM GB/s (1 GPU)", "GB/s"
+    elif getattr(wl, "backward", False):
+        achieved = flops / (ms * 1e-3) / 1e12
+        value = achieved
+        roof = metrics.roofline("mfma", achieved, metrics.MI355X_BF16_DENSE_TFLOPS, "TFLOP/s", traffic)
+        metric, unit = "packed GQA attn bwd mask-effective TFLOP/s + % bf16 MFMA peak (1 GPU)", "TFLOP/s"
+        config["pct_bf16_mfma_peak"] = 100.0 * achieved / metrics.MI355X_BF16_DENSE_TFLOPS
     elif sparse:
         achieved = work / (ms * 1e-3) / 1e9
         value = achieved
@@ -305,7 +365,9 @@ def main() -> int:
         line["config"]["tflops"] = flops / (ms * 1e-3) / 1e12
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = (cpu_baseline_vproj(inp) if vproj else
-                                cpu_baseline_sparse(inp) if sparse else cpu_baseline_dense(inp))
+                                cpu_baseline_sparse(inp) if sparse else
+                                cpu_baseline_dense_bwd(inp) if getattr(wl, "backward", False) else
+                                cpu_baseline_dense(inp))
     print(json.dumps(line), flush=True)
     return 0
 

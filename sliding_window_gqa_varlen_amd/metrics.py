@@ -43,6 +43,11 @@ def dense_flops(lengths: Sequence[int], window: int, Hq: int, D: int) -> int:
     return 4 * D * Hq * dense_allowed_pairs(lengths, window)
 
 
+def dense_bwd_flops(lengths: Sequence[int], window: int, Hq: int, D: int) -> int:
+    """Backward work per allowed pair and head: recompute q.k, then dout.v, dv, dq, dk (2 D each)."""
+    return 10 * D * Hq * dense_allowed_pairs(lengths, window)
+
+
 def dense_min_bytes(T: int, Hq: int, Hkv: int, D: int, elem_bytes: int, n_docs: int,
                     with_lse: bool = True, with_sinks: bool = False) -> int:
     b = elem_bytes * D * T * (2 * Hq + 2 * Hkv)

@@ -48,7 +48,7 @@ STREAM_Q, STREAM_K, STREAM_V, STREAM_SINK, STREAM_IDX, STREAM_LATENT, STREAM_KPE
 # ---------------------------------------------------------------------------
 @dataclasses.dataclass(frozen=True)
 class DenseWorkload:
-    """One packed varlen GQA forward problem."""
+    """One packed varlen GQA problem (the forward, or with ``backward`` its gradients)."""
 
     name: str
     dtype: str  # "f32" or "bf16"
@@ -63,6 +63,7 @@ class DenseWorkload:
     doc_dist: Optional[tuple] = None  # ("uniform"|"loguniform", a, b)
     rms_norm_qk: bool = False
     sinks: bool = False
+    backward: bool = False  # measure varlen_attn_bwd (dout from stream 9) instead of the forward
 
     def with_tokens(self, T: int, name: Optional[str] = None) -> "DenseWorkload":
         """Same recipe at another token count (document lengths capped at T)."""
@@ -129,11 +130,17 @@ class ValueProjWorkload:
     seed: int
 
 
-# Variants measured beside the five: dense full-causal GQA with head_dim 256 (the packed
+# Variants measured beside the five: the backward of the two head_dim-128 bf16 workloads (same
+# inputs, dout from its own stream), dense full-causal GQA with head_dim 256 (the packed
 # documents of the 8192-token workload, half its heads), the sparse workload without the
 # rotary part (NoPE, same documents and index rows), and the value projection at the sparse
 # workload's shape (its attention output feeds that step).
 EXTRA_WORKLOADS = (
+    DenseWorkload("causal_gqa_bwd_bf16_t8192", "bf16", T=8192, Hq=32, Hkv=8, D=128, window=0,
+                  scale=1.0 / math.sqrt(128.0), seed=1, doc_dist=("uniform", 128, 2048), backward=True),
+    DenseWorkload("swa1024_gqa_bwd_bf16_t32768", "bf16", T=32768, Hq=32, Hkv=4, D=128, window=1024,
+                  scale=1.0 / math.sqrt(128.0), seed=2, doc_dist=("uniform", 512, 8192), rms_norm_qk=True,
+                  backward=True),
     DenseWorkload("causal_gqa_d256_bf16_t8192", "bf16", T=8192, Hq=16, Hkv=4, D=256, window=0,
                   scale=1.0 / 16.0, seed=1, doc_dist=("uniform", 128, 2048)),
     SparseWorkload("sparse_mla_nope_bf16_t16384", T=16384, H=128, d_latent=512, d_rope=0, topk=2048,
