@@ -42,6 +42,9 @@ constexpr int kQF = kBD / 16;      // k-steps of 16 coordinates
 constexpr int kDB = kBD / 32;      // 32-row output blocks
 constexpr int kTileUnits = 64 * kU;
 constexpr int kTK = 128;           // keys per dk/dv workgroup
+#ifndef SWA_BWD_AHEAD
+#define SWA_BWD_AHEAD 8
+#endif
 
 __device__ __forceinline__ int rt_key(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 __device__ __forceinline__ int row_key(int r) { return r & 15; }
@@ -311,6 +314,93 @@ __device__ __forceinline__ bool decode_key_tile(const DenseBwdParams& p, KeyTile
   return true;
 }
 
+// One 64-query x 32-key tile of the dk/dv kernel as two fenced instruction streams (the
+// emitted order is the program order; operand fragments are read kAhead MFMAs ahead):
+//  1. S = Q K^T and dP = dO V^T (32 MFMAs, the two query blocks alternating); the
+//     probabilities P = exp2(S c2 - lse log2 e) of the tile run in the dP slots.
+//  2. dV^T += dO^T P and dK^T += Q^T dS (32 MFMAs); dS = P (dP - delta) runs in the dV slots.
+// Rows of the tile are queries; `qoff` = first query - this lane's key, `eoff` = document end -
+// key (the mask of MASK tiles: 0 <= query - key, query < end, and query - key < W when W > 0).
+template <bool MASK>
+__device__ __forceinline__ void dkdv_tile(const u32x4* qb, const u32x4* ob, const float* lb, const float* db,
+                                          const bf16x8 (&kf)[kQF], const bf16x8 (&vf)[kQF], int raddr,
+                                          const TrOffsets& to, float c2, f32x16 (&dk)[kDB], f32x16 (&dv)[kDB],
+                                          int qoff, int eoff, int W, int h2) {
+  constexpr int kAhead = SWA_BWD_AHEAD;
+  bf16x8 frag[64];
+  auto read = [&](int f) {
+    if (f < 32) {  // S (f < 16) or dP: query block f & 1, k-step (f >> 1) & 7
+      frag[f] = row_frag(f < 16 ? qb : ob, raddr, f & 1, (f >> 1) & 7);
+    } else {       // dV (f < 48) or dK: k-step (f >> 2) & 3, output block f & 3
+      frag[f] = tr_frag(f < 48 ? ob : qb, to, (f >> 2) & 3, f & 3);
+    }
+  };
+  f32x4 l4[8], d4[8];  // lse and delta of query rows 32 b + 8 j + 4 h2 + (0..3), index 4 b + j
+  f32x16 sc[2], dp[2];
+  bf16x8 pb[4], sb[4];
+  __builtin_amdgcn_s_setprio(1);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): nothing older in flight, later waits count exactly
+  // rows of group x: 32 (x >> 2) + 8 (x & 3) + 4 h2 .. + 3; lse now, delta late in stream 1
+  auto rows = [&](int x) { return 32 * (x >> 2) + 8 * (x & 3) + 4 * h2; };
+#pragma unroll
+  for (int x = 0; x < 8; ++x) l4[x] = *(const f32x4*)(lb + rows(x));
+#pragma unroll
+  for (int f = 0; f < kAhead; ++f) read(f);
+  __builtin_amdgcn_sched_barrier(0);
+  sc[0] = sc[1] = dp[0] = dp[1] = f32x16{};
+  // stream 1a: S (16 MFMAs)
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    sc[i & 1] = mfma_bf16_32x32x16(frag[i], kf[i >> 1], sc[i & 1]);
+    read(i + kAhead);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // stream 1b: dP (16 MFMAs) with the probabilities of S, two per slot
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    dp[i & 1] = mfma_bf16_32x32x16(frag[16 + i], vf[i >> 1], dp[i & 1]);
+    read(16 + i + kAhead);
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int x = 2 * i + e;  // element x of the tile's 32: block x >> 4, accumulator x & 15
+      const int bb = x >> 4, a = x & 15;
+      float pr = fast_exp2(__builtin_fmaf(sc[bb][a], c2, l4[x >> 2][a & 3] * -kLog2e));
+      if constexpr (MASK) {
+        const int d = qoff + 32 * bb + 8 * (a >> 2) + 4 * h2 + (a & 3);  // query - key
+        pr = (d >= 0 && d < eoff && (W == 0 || d < W)) ? pr : 0.f;
+      }
+      sc[bb][a] = pr;
+      asm volatile("" : "+v"(sc[bb][a]));  // this slot's probabilities stay in this slot
+      if ((x & 7) == 7) pb[x >> 3] = pack_ks(sc, x >> 3);
+    }
+    if (i >= 8) d4[i - 8] = *(const f32x4*)(db + rows(i - 8));
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // stream 2a: dV^T += dO^T P (16 MFMAs) with dS, two elements per slot
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    dv[i & 3] = mfma_bf16_32x32x16(frag[32 + i], pb[i >> 2], dv[i & 3]);
+    read(32 + i + kAhead);
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int x = 2 * i + e;
+      const int bb = x >> 4, a = x & 15;
+      dp[bb][a] = sc[bb][a] * (dp[bb][a] - d4[x >> 2][a & 3]);
+      asm volatile("" : "+v"(dp[bb][a]));
+      if ((x & 7) == 7) sb[x >> 3] = pack_ks(dp, x >> 3);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // stream 2b: dK^T += Q^T dS (16 MFMAs)
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    dk[i & 3] = mfma_bf16_32x32x16(frag[48 + i], sb[i >> 2], dk[i & 3]);
+    if (48 + i + kAhead < 64) read(48 + i + kAhead);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  __builtin_amdgcn_s_setprio(0);
+}
+
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(DenseBwdParams p) {
   __shared__ u32x4 q0[kTileUnits];
   __shared__ u32x4 q1[kTileUnits];
@@ -381,47 +471,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(DenseBwdParams p)
     const int i0 = w.k0 + 64 * (it % n_qt);
     // wave-uniform: skip tiles none of whose queries sees this wave's keys
     if (!has_keys || i0 + 63 < kw0 || (W != 0 && i0 > kw0 + 31 + W - 1)) return;
-    f32x16 sc[2], dp[2];
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      sc[b] = f32x16{};
-      dp[b] = f32x16{};
-#pragma unroll
-      for (int s = 0; s < kQF; ++s) sc[b] = mfma_bf16_32x32x16(row_frag(qb, raddr, b, s), kf[s], sc[b]);
-#pragma unroll
-      for (int s = 0; s < kQF; ++s) dp[b] = mfma_bf16_32x32x16(row_frag(ob, raddr, b, s), vf[s], dp[b]);
-    }
     const bool need_mask = !(i0 >= kw0 + 31 && i0 + 63 < e_doc && (W == 0 || i0 + 63 - kw0 < W));
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int rq = 32 * b + 8 * jj + 4 * h2;  // query rows rq .. rq + 3 of the tile
-        const f32x4 l4 = *(const f32x4*)(lb + rq);
-        const f32x4 d4 = *(const f32x4*)(db + rq);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int a = 4 * jj + e;
-          float pr = fast_exp2(__builtin_fmaf(sc[b][a], c2, -l4[e] * kLog2e));
-          if (need_mask) {
-            const int i = i0 + rq + e;
-            const bool ok = key <= i && i < e_doc && (W == 0 || i - key < W);
-            pr = ok ? pr : 0.f;
-          }
-          sc[b][a] = pr;
-          dp[b][a] = pr * (dp[b][a] - d4[e]);
-        }
-      }
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const bf16x8 pb = pack_ks(sc, ks);
-      const bf16x8 sb = pack_ks(dp, ks);
-#pragma unroll
-      for (int d = 0; d < kDB; ++d) {
-        dv[d] = mfma_bf16_32x32x16(tr_frag(ob, to, ks, d), pb, dv[d]);
-        dk[d] = mfma_bf16_32x32x16(tr_frag(qb, to, ks, d), sb, dk[d]);
-      }
-    }
+    if (need_mask)
+      dkdv_tile<true>(qb, ob, lb, db, kf, vf, raddr, to, c2, dk, dv, i0 - key, e_doc - key, W, h2);
+    else
+      dkdv_tile<false>(qb, ob, lb, db, kf, vf, raddr, to, c2, dk, dv, i0 - key, e_doc - key, W, h2);
   };
 
   issue(0, q0, o0, ls0, dl0);
