@@ -41,6 +41,7 @@ TRAFFIC_FILES = {
     "causal_gqa_d256_bf16_t8192": "profiles/dense_fwd_causal_gqa_d256_bf16_t8192_traffic.txt",
     "causal_gqa_bwd_bf16_t8192": "profiles/dense_bwd_causal_gqa_bf16_t8192_traffic.txt",
     "swa1024_gqa_bwd_bf16_t32768": "profiles/dense_bwd_swa1024_gqa_bf16_t32768_traffic.txt",
+    "swa128_sink_gqa_bwd_bf16_t65536": "profiles/dense_bwd_swa128_sink_gqa_bf16_t65536_traffic.txt",
     "sparse_mla_bf16_t16384": "profiles/sparse_mla_fwd_bf16_t16384_traffic.txt",
     "sparse_mla_nope_bf16_t16384": "profiles/sparse_mla_fwd_nope_bf16_t16384_traffic.txt",
     "mla_value_proj_bf16_t16384": "profiles/mla_value_proj_bf16_t16384_traffic.txt",

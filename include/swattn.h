@@ -148,7 +148,7 @@ int32_t varlen_attn_fwd(const swa_tensor* q, const swa_tensor* k, const swa_tens
  *   delta              device f32 [T, Hq] contiguous, written (a workspace the caller
  *                      owns: the library allocates nothing)
  *   stream             hipStream_t; four kernels are enqueued in order
- * Supported: D = 128, T * Hq < 2^30. Errors: as varlen_attn_fwd; SWA_ERR_NULL when lse,
+ * Supported: D in {64, 128}, T * Hq < 2^30. Errors: as varlen_attn_fwd; SWA_ERR_NULL when lse,
  * delta or (with sinks) dsinks is NULL; SWA_ERR_ARG when a gradient aliases an input or
  * another gradient. Arithmetic: bf16 matrix products (P and dS rounded to bf16 as
  * operands), f32 accumulation, one rounding of each gradient.

@@ -150,7 +150,7 @@ def varlen_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torc
                     dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
                     dv: Optional[torch.Tensor] = None, dsinks: Optional[torch.Tensor] = None,
                     delta: Optional[torch.Tensor] = None, stream=None):
-    """Backward of varlen_attn_fwd (bf16, head_dim 128) from its out and lse.
+    """Backward of varlen_attn_fwd (bf16, head_dim 64 or 128) from its out and lse.
 
     Returns (dq, dk, dv, dsinks) — dsinks is None without sinks.  ``delta`` is a
     [T, Hq] fp32 workspace (allocated here when not given).

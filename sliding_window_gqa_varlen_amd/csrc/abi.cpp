@@ -181,7 +181,8 @@ int32_t varlen_attn_bwd(const swa_tensor* q, const swa_tensor* k, const swa_tens
   if (Hq <= 0 || Hkv <= 0) return fail(SWA_ERR_SHAPE, "head counts must be positive");
   if (Hq % Hkv != 0) return fail(SWA_ERR_SHAPE, "Hq (%lld) must be a multiple of Hkv (%lld)",
                                  (long long)Hq, (long long)Hkv);
-  if (D != 128) return fail(SWA_ERR_UNSUPPORTED, "backward head_dim %lld not supported (128)", (long long)D);
+  if (D != 64 && D != 128)
+    return fail(SWA_ERR_UNSUPPORTED, "backward head_dim %lld not supported (64 or 128)", (long long)D);
   if (T * Hq >= (int64_t)1 << 30) return fail(SWA_ERR_UNSUPPORTED, "T * Hq too large");
   for (const swa_tensor* t : {q, k, v, dout})
     if (t->stride[0] >= (int64_t)1 << 24) return fail(SWA_ERR_UNSUPPORTED, "token strides must be below 2^24 elements");

@@ -1,5 +1,5 @@
 // Packed variable-length causal / sliding-window GQA attention backward for gfx950 (bf16,
-// head_dim 128).
+// head_dim 64 or 128).
 //
 // Operation: the gradients of a loss through `out` of the forward in dense_fwd.hip
 // (MuseMagiPlan.attention on the muse_spark magi_cp page, FlintMagiPlan.attention on the
@@ -26,9 +26,10 @@
 //    staged Q and dO tiles.  All heads of the group accumulate in registers: GQA needs no
 //    reduction pass.
 //  * K tiles (dq kernel) and Q / dO tiles (dk/dv kernel) are read both row-wise and
-//    transposed, so their 16-byte units are swizzled with rt_key(r) (row bits 0-1 into unit
-//    bits 2-3, row bits 2-3 into unit bits 0-1), which keeps both access patterns free of
-//    bank conflicts.  V tiles (dq kernel) are only read row-wise (unit ^ (r & 15)).
+//    transposed, so their 16-byte units are swizzled with rt_key(r), which keeps both access
+//    patterns free of bank conflicts: for 256-byte rows (D = 128) row bits 0-1 go to unit bits
+//    2-3 and row bits 2-3 to unit bits 0-1; for 128-byte rows (D = 64, two rows per bank line)
+//    m = (r >> 1) & 7 goes to m ^ ((m & 1) << 2).  V tiles (dq kernel) are only read row-wise.
 //  * Tiles travel HBM -> LDS by buffer_load ... lds into two statically named buffers per
 //    operand (loop unrolled by two): the next tile is in flight while this one is used.
 #include "dense_common.h"
@@ -36,35 +37,49 @@
 namespace swa {
 namespace {
 
-constexpr int kBD = 128;           // head_dim of this path
-constexpr int kU = kBD / 8;        // 16-byte units per row
-constexpr int kQF = kBD / 16;      // k-steps of 16 coordinates
-constexpr int kDB = kBD / 32;      // 32-row output blocks
-constexpr int kTileUnits = 64 * kU;
 constexpr int kTK = 128;           // keys per dk/dv workgroup
 #ifndef SWA_BWD_AHEAD
 #define SWA_BWD_AHEAD 8
 #endif
 
-__device__ __forceinline__ int rt_key(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
-__device__ __forceinline__ int row_key(int r) { return r & 15; }
+template <int D>
+struct Bw {
+  static constexpr int U = D / 8;              // 16-byte units per row
+  static constexpr int QF = D / 16;            // k-steps of 16 coordinates
+  static constexpr int DB = D / 32;            // 32-row output blocks
+  static constexpr int TileUnits = 64 * U;     // a 64-row tile
+  static constexpr int NS = 2 * QF;            // MFMAs of S (or dP) for two 32-row blocks
+  static constexpr int NV = 4 * DB;            // MFMAs of dV^T (or dK^T) over 64 rows
+  static constexpr int HiXor = D == 128 ? 2 : 4;  // rt_key(r + 8) = rt_key(r) ^ HiXor for r < 8
+};
+template <int D>
+__device__ __forceinline__ int rt_key(int r) {
+  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return ((r >> 1) & 7) ^ (((r >> 1) & 1) << 2);
+}
+template <int D>
+__device__ __forceinline__ int row_key(int r) {
+  if constexpr (D == 128) return r & 15;
+  else return (r >> 1) & 7;
+}
 
-// 64 rows (r0 .. r0 + 63, clamped to r_last >= r0) of 128 bf16 each into buf; logical unit u of
-// row r lands at physical unit u ^ key(r).  Four transfers per wave.
-template <bool RT>
+// 64 rows (r0 .. r0 + 63, clamped to r_last >= r0) of D bf16 each into buf; logical unit u of
+// row r lands at physical unit u ^ key(r).  U / 4 transfers of 64 units per wave.
+template <int D, bool RT>
 __device__ __forceinline__ void dma_rows64(const __bf16* base, int64_t st, int r0, int r_last, u32x4* buf, int wave,
                                            int lane_in) {
+  constexpr int U = Bw<D>::U, R = 64 / U;  // rows per 64-unit block
   const int lane = opaque(lane_in);
   const __amdgpu_buffer_rsrc_t rsrc =
       __builtin_amdgcn_make_buffer_rsrc((void*)(base + (int64_t)r0 * st), (short)0, -1, kBufferWord3);
   const uint32_t stb = (uint32_t)st * 2u;
   const int lim = r_last - r0;
-  const int lr = lane >> 4, lp = lane & 15;
+  const int lr = lane / U, lp = lane % U;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int blk = i * 4 + wave;  // wave-uniform block of 4 rows
-    const int r = blk * 4 + lr;
-    const int cu = lp ^ (RT ? rt_key(r) : row_key(r));
+  for (int i = 0; i < U / 4; ++i) {
+    const int blk = i * 4 + wave;  // wave-uniform block of R rows
+    const int r = blk * R + lr;
+    const int cu = lp ^ (RT ? rt_key<D>(r) : row_key<D>(r));
     u32x4* dst = buf + __builtin_amdgcn_readfirstlane(blk * 64);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)dst, 16, (uint32_t)min(r, lim) * stb + (uint32_t)cu * 16u,
                                              0, 0, 0);
@@ -80,34 +95,40 @@ __device__ __forceinline__ void dma_rowvals(const float* base, int Hq, int h, in
 }
 
 // Byte offset of the A-operand fragment of rows 32 blk + n, k-step s, in a row-swizzled tile:
-// unit (2 s + h2) ^ key(n) = (h2 ^ key(n)) ^ 2 s, i.e. raddr ^ 32 s.
+// unit (2 s + h2) ^ key(n) = (h2 ^ key(n)) ^ 2 s, i.e. raddr ^ 32 s with
+// raddr = n * U * 16 + ((h2 ^ key(n)) << 4).
+template <int D>
 __device__ __forceinline__ const bf16x8& row_frag(const u32x4* buf, int raddr, int blk, int s) {
-  return *(const bf16x8*)((const char*)buf + ((raddr ^ (32 * s)) + blk * 32 * kU * 16));
+  return *(const bf16x8*)((const char*)buf + ((raddr ^ (32 * s)) + blk * 32 * Bw<D>::U * 16));
 }
 
 // Transposed A-operand reads (ds_read_b64_tr_b16) of an rt_key tile: lane j of a 16-lane group
 // reads rows r0 = 4 h2 + j / 4 (+ 16 ks) and r0 + 8, 8-byte half (j & 1) of logical unit
-// 4 d + 2 dh + ((j & 3) >> 1).  key(r0 + 8) = key(r0) ^ 2.
+// 4 d + 2 dh + ((j & 3) >> 1).
+template <int D>
 struct TrOffsets {
-  int lo[kDB], hi[kDB];
+  int lo[Bw<D>::DB], hi[Bw<D>::DB];
 };
-__device__ __forceinline__ TrOffsets tr_offsets(int lane) {
+template <int D>
+__device__ __forceinline__ TrOffsets<D> tr_offsets(int lane) {
+  using B = Bw<D>;
   const int j16 = lane & 15, dh = (lane >> 4) & 1, h2 = lane >> 5;
   const int r0 = 4 * h2 + (j16 >> 2);
-  const int k0 = rt_key(r0);
+  const int k0 = rt_key<D>(r0);
   const int sub = (j16 & 3) >> 1;
   const int half = (j16 & 1) * 4;
-  TrOffsets t;
+  TrOffsets<D> t;
 #pragma unroll
-  for (int d = 0; d < kDB; ++d) {
+  for (int d = 0; d < B::DB; ++d) {
     const int u = 4 * d + 2 * dh + sub;
-    t.lo[d] = ((r0 * kU + (u ^ k0)) * 8 + half) * 2;
-    t.hi[d] = (((r0 + 8) * kU + (u ^ k0 ^ 2)) * 8 + half) * 2;
+    t.lo[d] = ((r0 * B::U + (u ^ k0)) * 8 + half) * 2;
+    t.hi[d] = (((r0 + 8) * B::U + (u ^ k0 ^ B::HiXor)) * 8 + half) * 2;
   }
   return t;
 }
-__device__ __forceinline__ bf16x8 tr_frag(const u32x4* buf, const TrOffsets& t, int ks, int d) {
-  const char* p = (const char*)buf + ks * 16 * kU * 16;
+template <int D>
+__device__ __forceinline__ bf16x8 tr_frag(const u32x4* buf, const TrOffsets<D>& t, int ks, int d) {
+  const char* p = (const char*)buf + ks * 16 * Bw<D>::U * 16;
   const bf16x4 lo4 = lds_read_tr4((const __bf16*)(p + t.lo[d]));
   const bf16x4 hi4 = lds_read_tr4((const __bf16*)(p + t.hi[d]));
   return __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -124,8 +145,9 @@ __device__ __forceinline__ bf16x8 pack_ks(const f32x16 (&x)[2], int ks) {
 // ======================================================================================
 // delta = <dout, out> per (token, head) row, and dsink
 // ======================================================================================
+template <int D>
 __global__ __launch_bounds__(kThreads) void bwd_delta_kernel(DenseBwdParams p) {
-  constexpr int LPR = kBD / 8;   // lanes per row (16 bytes each)
+  constexpr int LPR = D / 8;     // lanes per row (16 bytes each)
   constexpr int RPW = 64 / LPR;  // rows per wave step
   const int n_rows = p.f.T * p.f.Hq;
   const int lane = threadIdx.x & 63;
@@ -172,19 +194,21 @@ __global__ __launch_bounds__(kThreads) void bwd_dsink_kernel(DenseBwdParams p) {
 // ======================================================================================
 // dq: query-parallel, the forward's tiles
 // ======================================================================================
+template <int D>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(DenseBwdParams p) {
-  __shared__ u32x4 k0[kTileUnits];
-  __shared__ u32x4 k1[kTileUnits];
-  __shared__ u32x4 v0[kTileUnits];
-  __shared__ u32x4 v1[kTileUnits];
+  using B = Bw<D>;
+  __shared__ u32x4 k0[B::TileUnits];
+  __shared__ u32x4 k1[B::TileUnits];
+  __shared__ u32x4 v0[B::TileUnits];
+  __shared__ u32x4 v1[B::TileUnits];
   const DenseFwdParams& f = p.f;
 
   Tile w;
   if (!decode_tile(f, w)) return;
   if (w.padding) {  // tokens outside every document receive no gradient
     const int n_rows = (w.t_end - w.t0) * w.HB;
-    for (int idx = threadIdx.x; idx < n_rows * kU; idx += kThreads) {
-      const int row = idx / kU, cu = idx - row * kU;
+    for (int idx = threadIdx.x; idx < n_rows * B::U; idx += kThreads) {
+      const int row = idx / B::U, cu = idx - row * B::U;
       const int t = w.t0 + row / w.HB, h = w.h0 + row % w.HB;
       *(u32x4*)((__bf16*)p.dq + (int64_t)t * p.dq_st + (int64_t)h * p.dq_sh + cu * 8) = u32x4{0, 0, 0, 0};
     }
@@ -192,12 +216,12 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(DenseBwdParams p) {
   }
   const Cols c = make_cols(f, w);
   const int tq = min(c.tq, w.t_end - 1);
-  bf16x8 qf[kQF], gf[kQF];
+  bf16x8 qf[B::QF], gf[B::QF];
   {
     const __bf16* qb = (const __bf16*)f.q + (int64_t)tq * f.q_st + (int64_t)c.hq * f.q_sh + 8 * c.h2;
     const __bf16* gb = (const __bf16*)p.dout + (int64_t)tq * p.do_st + (int64_t)c.hq * p.do_sh + 8 * c.h2;
 #pragma unroll
-    for (int s = 0; s < kQF; ++s) {
+    for (int s = 0; s < B::QF; ++s) {
       qf[s] = *(const bf16x8*)(qb + 16 * s);
       gf[s] = *(const bf16x8*)(gb + 16 * s);
     }
@@ -207,13 +231,13 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(DenseBwdParams p) {
   const float c2 = f.c2;
   const __bf16* kbase = (const __bf16*)f.k + (int64_t)w.g * f.k_sh;
   const __bf16* vbase = (const __bf16*)f.v + (int64_t)w.g * f.v_sh;
-  const int kraddr = c.n * kU * 16 + ((c.h2 ^ rt_key(c.n)) << 4);
-  const int vraddr = c.n * kU * 16 + ((c.h2 ^ row_key(c.n)) << 4);
-  const TrOffsets to = tr_offsets(c.lane);
+  const int kraddr = c.n * B::U * 16 + ((c.h2 ^ rt_key<D>(c.n)) << 4);
+  const int vraddr = c.n * B::U * 16 + ((c.h2 ^ row_key<D>(c.n)) << 4);
+  const TrOffsets<D> to = tr_offsets<D>(c.lane);
 
-  f32x16 acc[kDB];
+  f32x16 acc[B::DB];
 #pragma unroll
-  for (int d = 0; d < kDB; ++d) acc[d] = f32x16{};
+  for (int d = 0; d < B::DB; ++d) acc[d] = f32x16{};
   const int nt = c.n_tiles;
   const int last = c.k_hi - 1;
 
@@ -225,9 +249,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(DenseBwdParams p) {
       sc[blk] = f32x16{};
       dp[blk] = f32x16{};
 #pragma unroll
-      for (int s = 0; s < kQF; ++s) sc[blk] = mfma_bf16_32x32x16(row_frag(kb_, kraddr, blk, s), qf[s], sc[blk]);
+      for (int s = 0; s < B::QF; ++s) sc[blk] = mfma_bf16_32x32x16(row_frag<D>(kb_, kraddr, blk, s), qf[s], sc[blk]);
 #pragma unroll
-      for (int s = 0; s < kQF; ++s) dp[blk] = mfma_bf16_32x32x16(row_frag(vb_, vraddr, blk, s), gf[s], dp[blk]);
+      for (int s = 0; s < B::QF; ++s) dp[blk] = mfma_bf16_32x32x16(row_frag<D>(vb_, vraddr, blk, s), gf[s], dp[blk]);
     }
     if (tile_needs_mask(c, kb)) mask_tile(sc, kb, c);
 #pragma unroll
@@ -241,24 +265,24 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(DenseBwdParams p) {
     for (int ks = 0; ks < 4; ++ks) {
       const bf16x8 sb = pack_ks(sc, ks);
 #pragma unroll
-      for (int d = 0; d < kDB; ++d) acc[d] = mfma_bf16_32x32x16(tr_frag(kb_, to, ks, d), sb, acc[d]);
+      for (int d = 0; d < B::DB; ++d) acc[d] = mfma_bf16_32x32x16(tr_frag<D>(kb_, to, ks, d), sb, acc[d]);
     }
   };
 
-  dma_rows64<true>(kbase, f.k_st, c.k_lo, last, k0, c.wave, c.lane);
-  dma_rows64<false>(vbase, f.v_st, c.k_lo, last, v0, c.wave, c.lane);
+  dma_rows64<D, true>(kbase, f.k_st, c.k_lo, last, k0, c.wave, c.lane);
+  dma_rows64<D, false>(vbase, f.v_st, c.k_lo, last, v0, c.wave, c.lane);
   int j = 0;
   for (; j + 1 < nt; j += 2) {
     wait_vm0();
     barrier_keep_loads();  // tile j landed for every wave; tile j - 1 fully consumed
-    dma_rows64<true>(kbase, f.k_st, c.k_lo + (j + 1) * kBN, last, k1, c.wave, c.lane);
-    dma_rows64<false>(vbase, f.v_st, c.k_lo + (j + 1) * kBN, last, v1, c.wave, c.lane);
+    dma_rows64<D, true>(kbase, f.k_st, c.k_lo + (j + 1) * kBN, last, k1, c.wave, c.lane);
+    dma_rows64<D, false>(vbase, f.v_st, c.k_lo + (j + 1) * kBN, last, v1, c.wave, c.lane);
     tile(k0, v0, c.k_lo + j * kBN);
     wait_vm0();
     barrier_keep_loads();
     if (j + 2 < nt) {
-      dma_rows64<true>(kbase, f.k_st, c.k_lo + (j + 2) * kBN, last, k0, c.wave, c.lane);
-      dma_rows64<false>(vbase, f.v_st, c.k_lo + (j + 2) * kBN, last, v0, c.wave, c.lane);
+      dma_rows64<D, true>(kbase, f.k_st, c.k_lo + (j + 2) * kBN, last, k0, c.wave, c.lane);
+      dma_rows64<D, false>(vbase, f.v_st, c.k_lo + (j + 2) * kBN, last, v0, c.wave, c.lane);
     }
     tile(k1, v1, c.k_lo + (j + 1) * kBN);
   }
@@ -271,7 +295,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(DenseBwdParams p) {
   if (c.tq < w.t_end) {
     __bf16* ob = (__bf16*)p.dq + (int64_t)c.tq * p.dq_st + (int64_t)c.hq * p.dq_sh + 4 * c.h2;
 #pragma unroll
-    for (int d = 0; d < kDB; ++d)
+    for (int d = 0; d < B::DB; ++d)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         f32x4 r;
@@ -321,18 +345,24 @@ __device__ __forceinline__ bool decode_key_tile(const DenseBwdParams& p, KeyTile
 //  2. dV^T += dO^T P and dK^T += Q^T dS (32 MFMAs); dS = P (dP - delta) runs in the dV slots.
 // Rows of the tile are queries; `qoff` = first query - this lane's key, `eoff` = document end -
 // key (the mask of MASK tiles: 0 <= query - key, query < end, and query - key < W when W > 0).
-template <bool MASK>
+template <int D, bool MASK>
 __device__ __forceinline__ void dkdv_tile(const u32x4* qb, const u32x4* ob, const float* lb, const float* db,
-                                          const bf16x8 (&kf)[kQF], const bf16x8 (&vf)[kQF], int raddr,
-                                          const TrOffsets& to, float c2, f32x16 (&dk)[kDB], f32x16 (&dv)[kDB],
-                                          int qoff, int eoff, int W, int h2) {
+                                          const bf16x8 (&kf)[Bw<D>::QF], const bf16x8 (&vf)[Bw<D>::QF], int raddr,
+                                          const TrOffsets<D>& to, float c2, f32x16 (&dk)[Bw<D>::DB],
+                                          f32x16 (&dv)[Bw<D>::DB], int qoff, int eoff, int W, int h2) {
+  using B = Bw<D>;
+  constexpr int NS = B::NS, NV = B::NV, NF = 2 * NS + 2 * NV;
+  constexpr int EPS = 32 / NS;  // probabilities per dP slot
+  constexpr int DPS = 32 / NV;  // dS elements per dV slot
   constexpr int kAhead = SWA_BWD_AHEAD;
-  bf16x8 frag[64];
+  static_assert(32 % NS == 0 && 32 % NV == 0 && NS >= 8, "slot shares");
+  bf16x8 frag[NF];
   auto read = [&](int f) {
-    if (f < 32) {  // S (f < 16) or dP: query block f & 1, k-step (f >> 1) & 7
-      frag[f] = row_frag(f < 16 ? qb : ob, raddr, f & 1, (f >> 1) & 7);
-    } else {       // dV (f < 48) or dK: k-step (f >> 2) & 3, output block f & 3
-      frag[f] = tr_frag(f < 48 ? ob : qb, to, (f >> 2) & 3, f & 3);
+    if (f < 2 * NS) {  // S (f < NS) or dP: query block f & 1, k-step (f % NS) >> 1
+      frag[f] = row_frag<D>(f < NS ? qb : ob, raddr, f & 1, (f % NS) >> 1);
+    } else {           // dV (first NV) or dK: k-step (i / DB) of 4, output block i % DB
+      const int i = f - 2 * NS;
+      frag[f] = tr_frag<D>(i < NV ? ob : qb, to, (i % NV) / B::DB, i % B::DB);
     }
   };
   f32x4 l4[8], d4[8];  // lse and delta of query rows 32 b + 8 j + 4 h2 + (0..3), index 4 b + j
@@ -348,21 +378,21 @@ __device__ __forceinline__ void dkdv_tile(const u32x4* qb, const u32x4* ob, cons
   for (int f = 0; f < kAhead; ++f) read(f);
   __builtin_amdgcn_sched_barrier(0);
   sc[0] = sc[1] = dp[0] = dp[1] = f32x16{};
-  // stream 1a: S (16 MFMAs)
+  // stream 1a: S (NS MFMAs, the two query blocks alternating)
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
+  for (int i = 0; i < NS; ++i) {
     sc[i & 1] = mfma_bf16_32x32x16(frag[i], kf[i >> 1], sc[i & 1]);
     read(i + kAhead);
     __builtin_amdgcn_sched_barrier(0);
   }
-  // stream 1b: dP (16 MFMAs) with the probabilities of S, two per slot
+  // stream 1b: dP (NS MFMAs) with the probabilities of S, EPS per slot
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    dp[i & 1] = mfma_bf16_32x32x16(frag[16 + i], vf[i >> 1], dp[i & 1]);
-    read(16 + i + kAhead);
+  for (int i = 0; i < NS; ++i) {
+    dp[i & 1] = mfma_bf16_32x32x16(frag[NS + i], vf[i >> 1], dp[i & 1]);
+    read(NS + i + kAhead);
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int x = 2 * i + e;  // element x of the tile's 32: block x >> 4, accumulator x & 15
+    for (int e = 0; e < EPS; ++e) {
+      const int x = EPS * i + e;  // element x of the tile's 32: block x >> 4, accumulator x & 15
       const int bb = x >> 4, a = x & 15;
       float pr = fast_exp2(__builtin_fmaf(sc[bb][a], c2, l4[x >> 2][a & 3] * -kLog2e));
       if constexpr (MASK) {
@@ -373,17 +403,17 @@ __device__ __forceinline__ void dkdv_tile(const u32x4* qb, const u32x4* ob, cons
       asm volatile("" : "+v"(sc[bb][a]));  // this slot's probabilities stay in this slot
       if ((x & 7) == 7) pb[x >> 3] = pack_ks(sc, x >> 3);
     }
-    if (i >= 8) d4[i - 8] = *(const f32x4*)(db + rows(i - 8));
+    if (i >= NS - 8) d4[i - (NS - 8)] = *(const f32x4*)(db + rows(i - (NS - 8)));
     __builtin_amdgcn_sched_barrier(0);
   }
-  // stream 2a: dV^T += dO^T P (16 MFMAs) with dS, two elements per slot
+  // stream 2a: dV^T += dO^T P (NV MFMAs) with dS, DPS elements per slot
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    dv[i & 3] = mfma_bf16_32x32x16(frag[32 + i], pb[i >> 2], dv[i & 3]);
-    read(32 + i + kAhead);
+  for (int i = 0; i < NV; ++i) {
+    dv[i % B::DB] = mfma_bf16_32x32x16(frag[2 * NS + i], pb[i / B::DB], dv[i % B::DB]);
+    read(2 * NS + i + kAhead);
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int x = 2 * i + e;
+    for (int e = 0; e < DPS; ++e) {
+      const int x = DPS * i + e;
       const int bb = x >> 4, a = x & 15;
       dp[bb][a] = sc[bb][a] * (dp[bb][a] - d4[x >> 2][a & 3]);
       asm volatile("" : "+v"(dp[bb][a]));
@@ -391,21 +421,23 @@ __device__ __forceinline__ void dkdv_tile(const u32x4* qb, const u32x4* ob, cons
     }
     __builtin_amdgcn_sched_barrier(0);
   }
-  // stream 2b: dK^T += Q^T dS (16 MFMAs)
+  // stream 2b: dK^T += Q^T dS (NV MFMAs)
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    dk[i & 3] = mfma_bf16_32x32x16(frag[48 + i], sb[i >> 2], dk[i & 3]);
-    if (48 + i + kAhead < 64) read(48 + i + kAhead);
+  for (int i = 0; i < NV; ++i) {
+    dk[i % B::DB] = mfma_bf16_32x32x16(frag[2 * NS + NV + i], sb[i / B::DB], dk[i % B::DB]);
+    if (2 * NS + NV + i + kAhead < NF) read(2 * NS + NV + i + kAhead);
     __builtin_amdgcn_sched_barrier(0);
   }
   __builtin_amdgcn_s_setprio(0);
 }
 
+template <int D>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(DenseBwdParams p) {
-  __shared__ u32x4 q0[kTileUnits];
-  __shared__ u32x4 q1[kTileUnits];
-  __shared__ u32x4 o0[kTileUnits];
-  __shared__ u32x4 o1[kTileUnits];
+  using B = Bw<D>;
+  __shared__ u32x4 q0[B::TileUnits];
+  __shared__ u32x4 q1[B::TileUnits];
+  __shared__ u32x4 o0[B::TileUnits];
+  __shared__ u32x4 o1[B::TileUnits];
   __shared__ f32x4 lsv[4][16];  // lse and delta rows of the two query-tile buffers (16-byte aligned)
   float* ls0 = (float*)lsv[0];
   float* ls1 = (float*)lsv[1];
@@ -417,8 +449,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(DenseBwdParams p)
   if (!decode_key_tile(p, w)) return;
   if (w.padding) {  // keys outside every document receive no gradient
     const int n_rows = w.k1 - w.k0;
-    for (int idx = threadIdx.x; idx < n_rows * kU; idx += kThreads) {
-      const int row = idx / kU, cu = idx - row * kU;
+    for (int idx = threadIdx.x; idx < n_rows * B::U; idx += kThreads) {
+      const int row = idx / B::U, cu = idx - row * B::U;
       const int64_t t = w.k0 + row;
       *(u32x4*)((__bf16*)p.dk + t * p.dk_st + (int64_t)w.g * p.dk_sh + cu * 8) = u32x4{0, 0, 0, 0};
       *(u32x4*)((__bf16*)p.dv + t * p.dv_st + (int64_t)w.g * p.dv_sh + cu * 8) = u32x4{0, 0, 0, 0};
@@ -434,20 +466,20 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(DenseBwdParams p)
   const int key = kw0 + n;           // this lane's key column
 
   // K and V rows of this lane's key as B operands: coordinates 16 s + 8 h2 .. + 7
-  bf16x8 kf[kQF], vf[kQF];
+  bf16x8 kf[B::QF], vf[B::QF];
   {
     const int kr = min(key, w.k1 - 1);
     const __bf16* kb = (const __bf16*)f.k + (int64_t)kr * f.k_st + (int64_t)w.g * f.k_sh + 8 * h2;
     const __bf16* vb = (const __bf16*)f.v + (int64_t)kr * f.v_st + (int64_t)w.g * f.v_sh + 8 * h2;
 #pragma unroll
-    for (int s = 0; s < kQF; ++s) {
+    for (int s = 0; s < B::QF; ++s) {
       kf[s] = *(const bf16x8*)(kb + 16 * s);
       vf[s] = *(const bf16x8*)(vb + 16 * s);
     }
   }
-  f32x16 dk[kDB], dv[kDB];
+  f32x16 dk[B::DB], dv[B::DB];
 #pragma unroll
-  for (int d = 0; d < kDB; ++d) {
+  for (int d = 0; d < B::DB; ++d) {
     dk[d] = f32x16{};
     dv[d] = f32x16{};
   }
@@ -455,15 +487,15 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(DenseBwdParams p)
   const int i_hi = W ? min(e_doc, w.k1 - 1 + W) : e_doc;
   const int n_qt = (i_hi - w.k0 + 63) / 64;
   const int n_it = f.G * n_qt;
-  const int raddr = n * kU * 16 + ((h2 ^ rt_key(n)) << 4);
-  const TrOffsets to = tr_offsets(lane);
+  const int raddr = n * B::U * 16 + ((h2 ^ rt_key<D>(n)) << 4);
+  const TrOffsets<D> to = tr_offsets<D>(lane);
   const float c2 = f.c2;
 
   auto issue = [&](int it, u32x4* qb, u32x4* ob, float* lb, float* db) {
     const int h = w.g * f.G + it / n_qt;
     const int i0 = w.k0 + 64 * (it % n_qt);
-    dma_rows64<true>((const __bf16*)f.q + (int64_t)h * f.q_sh, f.q_st, i0, i_hi - 1, qb, wave, lane);
-    dma_rows64<true>((const __bf16*)p.dout + (int64_t)h * p.do_sh, p.do_st, i0, i_hi - 1, ob, wave, lane);
+    dma_rows64<D, true>((const __bf16*)f.q + (int64_t)h * f.q_sh, f.q_st, i0, i_hi - 1, qb, wave, lane);
+    dma_rows64<D, true>((const __bf16*)p.dout + (int64_t)h * p.do_sh, p.do_st, i0, i_hi - 1, ob, wave, lane);
     if (wave == 0) dma_rowvals(f.lse, f.Hq, h, i0, i_hi - 1, lb, lane);
     if (wave == 1) dma_rowvals(p.delta, f.Hq, h, i0, i_hi - 1, db, lane);
   };
@@ -473,9 +505,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(DenseBwdParams p)
     if (!has_keys || i0 + 63 < kw0 || (W != 0 && i0 > kw0 + 31 + W - 1)) return;
     const bool need_mask = !(i0 >= kw0 + 31 && i0 + 63 < e_doc && (W == 0 || i0 + 63 - kw0 < W));
     if (need_mask)
-      dkdv_tile<true>(qb, ob, lb, db, kf, vf, raddr, to, c2, dk, dv, i0 - key, e_doc - key, W, h2);
+      dkdv_tile<D, true>(qb, ob, lb, db, kf, vf, raddr, to, c2, dk, dv, i0 - key, e_doc - key, W, h2);
     else
-      dkdv_tile<false>(qb, ob, lb, db, kf, vf, raddr, to, c2, dk, dv, i0 - key, e_doc - key, W, h2);
+      dkdv_tile<D, false>(qb, ob, lb, db, kf, vf, raddr, to, c2, dk, dv, i0 - key, e_doc - key, W, h2);
   };
 
   issue(0, q0, o0, ls0, dl0);
@@ -500,7 +532,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(DenseBwdParams p)
     __bf16* kb = (__bf16*)p.dk + (int64_t)key * p.dk_st + (int64_t)w.g * p.dk_sh + 4 * h2;
     __bf16* vb = (__bf16*)p.dv + (int64_t)key * p.dv_st + (int64_t)w.g * p.dv_sh + 4 * h2;
 #pragma unroll
-    for (int d = 0; d < kDB; ++d)
+    for (int d = 0; d < B::DB; ++d)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         f32x4 rk, rv;
@@ -523,21 +555,29 @@ void dense_bwd_plan(DenseBwdParams& p) {
   p.kv_n_work = p.f.Hkv * p.kv_n_vtiles;
 }
 
-hipError_t dense_bwd_launch(const DenseBwdParams& p, int D, hipStream_t stream) {
-  if (D != kBD) return hipErrorInvalidValue;
-  if (p.f.T <= 0) return hipSuccess;
+namespace {
+template <int D>
+hipError_t bwd_launch(const DenseBwdParams& p, hipStream_t stream) {
   const int64_t rows = (int64_t)p.f.T * p.f.Hq;
-  const int64_t rows_per_block = (kThreads / 64) * (64 / (kBD / 8));
+  const int64_t rows_per_block = (kThreads / 64) * (64 / (D / 8));
   int64_t gd = (rows + rows_per_block - 1) / rows_per_block;
   gd = gd > 8192 ? 8192 : gd;
-  hipLaunchKernelGGL(bwd_delta_kernel, dim3((unsigned)gd), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL(bwd_delta_kernel<D>, dim3((unsigned)gd), dim3(kThreads), 0, stream, p);
   if (p.f.sinks != nullptr && p.dsinks != nullptr)
     hipLaunchKernelGGL(bwd_dsink_kernel, dim3((unsigned)p.f.Hq), dim3(kThreads), 0, stream, p);
   const int64_t gq = dense_fwd_grid(p.f);
-  if (gq > 0) hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)gq), dim3(kThreads), 0, stream, p);
+  if (gq > 0) hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3((unsigned)gq), dim3(kThreads), 0, stream, p);
   const int64_t gk = ((int64_t)p.kv_n_work + kXcds - 1) / kXcds * kXcds;
-  if (gk > 0) hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)gk), dim3(kThreads), 0, stream, p);
+  if (gk > 0) hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3((unsigned)gk), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
+}
+}  // namespace
+
+hipError_t dense_bwd_launch(const DenseBwdParams& p, int D, hipStream_t stream) {
+  if (p.f.T <= 0) return hipSuccess;
+  if (D == 128) return bwd_launch<128>(p, stream);
+  if (D == 64) return bwd_launch<64>(p, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace swa

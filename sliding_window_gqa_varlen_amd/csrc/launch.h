@@ -36,7 +36,7 @@ int64_t dense_fwd_grid(const DenseFwdParams& p);
 void dense_fwd_plan(DenseFwdParams& p);
 hipError_t dense_fwd_launch(const DenseFwdParams& p, Dtype dt, int D, hipStream_t stream);
 
-// Packed varlen GQA backward (bf16, head_dim 128). `f` carries the forward's geometry and
+// Packed varlen GQA backward (bf16, head_dim 64 or 128). `f` carries the forward's geometry and
 // inputs (q, k, v, out = the forward output, lse = the forward LSE, read only); strides in
 // elements.
 struct DenseBwdParams {

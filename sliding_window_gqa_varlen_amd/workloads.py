@@ -130,7 +130,7 @@ class ValueProjWorkload:
     seed: int
 
 
-# Variants measured beside the five: the backward of the two head_dim-128 bf16 workloads (same
+# Variants measured beside the five: the backward of the three bf16 workloads (same
 # inputs, dout from its own stream), dense full-causal GQA with head_dim 256 (the packed
 # documents of the 8192-token workload, half its heads), the sparse workload without the
 # rotary part (NoPE, same documents and index rows), and the value projection at the sparse
@@ -141,6 +141,8 @@ EXTRA_WORKLOADS = (
     DenseWorkload("swa1024_gqa_bwd_bf16_t32768", "bf16", T=32768, Hq=32, Hkv=4, D=128, window=1024,
                   scale=1.0 / math.sqrt(128.0), seed=2, doc_dist=("uniform", 512, 8192), rms_norm_qk=True,
                   backward=True),
+    DenseWorkload("swa128_sink_gqa_bwd_bf16_t65536", "bf16", T=65536, Hq=64, Hkv=8, D=64, window=128,
+                  scale=1.0 / 8.0, seed=3, doc_dist=("loguniform", 64, 16384), sinks=True, backward=True),
     DenseWorkload("causal_gqa_d256_bf16_t8192", "bf16", T=8192, Hq=16, Hkv=4, D=256, window=0,
                   scale=1.0 / 16.0, seed=1, doc_dist=("uniform", 128, 2048)),
     SparseWorkload("sparse_mla_nope_bf16_t16384", T=16384, H=128, d_latent=512, d_rope=0, topk=2048,

@@ -250,3 +250,52 @@ def test_value_proj_empty_problem_is_a_no_op(lib):
     assert call_vproj(lib, vproj_args(T=0)) == SWA_OK
     a = vproj_args(T=0)
     assert binding.mla_value_proj(a["o"], a["w"], stream=0).shape == (0, 4, 128)
+
+
+# ---------------------------------------------------------------- backward argument checks
+def bwd_args(T=16, Hq=4, Hkv=2, D=128, dtype=torch.bfloat16):
+    a = {n: torch.zeros(T, Hq, D, dtype=dtype) for n in ("q", "out", "dout", "dq")}
+    a.update({n: torch.zeros(T, Hkv, D, dtype=dtype) for n in ("k", "v", "dk", "dv")})
+    a.update(lse=torch.zeros(T, Hq), delta=torch.zeros(T, Hq), cu=torch.tensor([0, T], dtype=torch.int32),
+             sinks=None, dsinks=None)
+    return a
+
+
+def call_bwd(lib, a, window=0, scale=0.125, lse="default", delta="default"):
+    d = {n: describe(a[n]) for n in ("q", "k", "v", "out", "dout", "dq", "dk", "dv")}
+    ptr = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    lse_p = ptr(a["lse"]) if lse == "default" else lse
+    delta_p = ptr(a["delta"]) if delta == "default" else delta
+    return lib.varlen_attn_bwd(*(ctypes.byref(d[n]) for n in ("q", "k", "v", "out", "dout")), lse_p,
+                               ptr(a["cu"]), 1, window, scale, ptr(a["sinks"]),
+                               *(ctypes.byref(d[n]) for n in ("dq", "dk", "dv")), ptr(a["dsinks"]), delta_p, None)
+
+
+def test_bwd_rejects_bad_arguments(lib):
+    assert call_bwd(lib, bwd_args(), lse=None) == SWA_ERR_NULL
+    assert call_bwd(lib, bwd_args(), delta=None) == SWA_ERR_NULL
+    a = bwd_args()
+    a["sinks"] = torch.zeros(4)
+    assert call_bwd(lib, a) == SWA_ERR_NULL  # dsinks required with sinks
+    assert call_bwd(lib, bwd_args(dtype=torch.float32)) == SWA_ERR_DTYPE
+    for D in (32, 256):
+        assert call_bwd(lib, bwd_args(D=D)) == SWA_ERR_UNSUPPORTED
+    a = bwd_args()
+    a["dk"] = torch.zeros(16, 4, 128, dtype=torch.bfloat16)
+    assert call_bwd(lib, a) == SWA_ERR_SHAPE
+    a = bwd_args()
+    a["dout"] = torch.zeros(15, 4, 128, dtype=torch.bfloat16)
+    assert call_bwd(lib, a) == SWA_ERR_SHAPE
+    assert call_bwd(lib, bwd_args(Hq=3, Hkv=2)) == SWA_ERR_SHAPE
+    assert call_bwd(lib, bwd_args(), window=-1) == SWA_ERR_ARG
+    assert call_bwd(lib, bwd_args(), scale=0.0) == SWA_ERR_ARG
+    a = bwd_args()
+    a["dq"] = a["q"]
+    assert call_bwd(lib, a) == SWA_ERR_ARG  # gradient aliases an input
+    a = bwd_args(Hq=2, Hkv=2)
+    a["dv"] = a["dk"]
+    assert call_bwd(lib, a) == SWA_ERR_ARG  # two gradients share storage
+
+
+def test_bwd_empty_problem_is_a_no_op(lib):
+    assert call_bwd(lib, bwd_args(T=0)) == SWA_OK

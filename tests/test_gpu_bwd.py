@@ -147,10 +147,11 @@ def check_all(got, ref, inp=None, do=None, window=None, out_given=None, lse_give
     assert np.all(np.abs(g - same_input) <= 1e-4 * np.maximum(1.0, (p * np.abs(delta_b)).sum(axis=0)))
 
 
+@pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("sinks", [False, True])
-def test_ragged_documents_and_padding_tail(gpu, sinks):
+def test_ragged_documents_and_padding_tail(gpu, sinks, D):
     lengths = [1, 31, 33, 63, 65, 127, 129, 2, 200]
-    inp = custom(lengths, T=sum(lengths) + 37, Hq=8, Hkv=2, window=0, sinks=sinks, seed=1 + sinks)
+    inp = custom(lengths, T=sum(lengths) + 37, Hq=8, Hkv=2, window=0, sinks=sinks, seed=1 + sinks, D=D)
     do = dout_for(inp, 3)
     got = run_bwd(inp, do)
     check_all(got, oracle_bwd(inp, do), inp, do)
@@ -158,18 +159,20 @@ def test_ragged_documents_and_padding_tail(gpu, sinks):
     assert np.all(got[0][T0:] == 0) and np.all(got[1][T0:] == 0) and np.all(got[2][T0:] == 0)
 
 
-@pytest.mark.parametrize("window", [1, 17, 64, 65, 100, 200])
-def test_windows_with_sinks(gpu, window):
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("window", [1, 17, 64, 65, 100, 128, 200])
+def test_windows_with_sinks(gpu, window, D):
     lengths = [300, 5, 129, 64]
-    inp = custom(lengths, T=sum(lengths), Hq=16, Hkv=2, window=window, sinks=True, seed=window)
+    inp = custom(lengths, T=sum(lengths), Hq=16, Hkv=2, window=window, sinks=True, seed=window, D=D)
     do = dout_for(inp, window)
     check_all(run_bwd(inp, do), oracle_bwd(inp, do), inp, do)
 
 
-@pytest.mark.parametrize("Hq,Hkv", [(4, 4), (6, 1), (12, 2), (40, 8), (64, 1)])
-def test_gqa_group_shapes(gpu, Hq, Hkv):
+@pytest.mark.parametrize("Hq,Hkv,D", [(4, 4, 128), (6, 1, 128), (12, 2, 128), (40, 8, 128), (64, 1, 128),
+                                     (6, 1, 64), (64, 8, 64)])
+def test_gqa_group_shapes(gpu, Hq, Hkv, D):
     lengths = [100, 37, 150]
-    inp = custom(lengths, T=287, Hq=Hq, Hkv=Hkv, window=50, sinks=True, seed=Hq + Hkv)
+    inp = custom(lengths, T=287, Hq=Hq, Hkv=Hkv, window=50, sinks=True, seed=Hq + Hkv, D=D)
     do = dout_for(inp, 7)
     check_all(run_bwd(inp, do), oracle_bwd(inp, do), inp, do)
 
@@ -194,7 +197,7 @@ def test_packed_documents_elementwise(gpu):
     check_all(run_bwd(inp, do), oracle_bwd(inp, do), inp, do)
 
 
-@pytest.mark.parametrize("idx", [1, 2])
+@pytest.mark.parametrize("idx", [1, 2, 3])
 def test_full_size_workloads_on_chosen_documents(gpu, idx):
     """The full-size workloads in the bench's launch configuration (out and lse from the GPU
     forward); the oracle recomputes whole documents (documents are independent), the smallest
