@@ -147,7 +147,8 @@ int32_t varlen_attn_fwd(const swa_tensor* q, const swa_tensor* k, const swa_tens
  *                      ignored
  *   delta              device f32 [T, Hq] contiguous, written (a workspace the caller
  *                      owns: the library allocates nothing)
- *   stream             hipStream_t; four kernels are enqueued in order
+ *   stream             hipStream_t; dq (which also writes delta), dsink (with sinks) and
+ *                      dk/dv kernels are enqueued in that order
  * Supported: D in {64, 128}, T * Hq < 2^30. Errors: as varlen_attn_fwd; SWA_ERR_NULL when lse,
  * delta or (with sinks) dsinks is NULL; SWA_ERR_ARG when a gradient aliases an input or
  * another gradient. Arithmetic: bf16 matrix products (P and dS rounded to bf16 as

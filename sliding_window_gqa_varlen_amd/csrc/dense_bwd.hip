@@ -11,13 +11,14 @@
 //   dsink_h = -sum_i exp(sink_h - lse_i) delta_i
 //
 // Design (MFMA 32x32x16 bf16, fp32 accumulation, no atomics, no scratch beyond `delta`):
-//  * delta kernel: one fp32 dot product per (token, head) row.
 //  * dsink kernel: one workgroup per head reduces over the tokens in a fixed order.
 //  * dq kernel (query-parallel): the forward's workgroup decomposition (per document, 128
 //    query columns = tokens x folded GQA heads, XCD-aware placement).  Per 64-key tile:
 //    S^T = K Q^T and dP^T = V dO^T with q and dout of the lane's column in registers, so
 //    P^T = exp2(S^T c2 - lse_col) and dS^T = P^T (dP^T - delta_col) are lane-local; then
 //    dQ^T += K^T dS^T with the K^T operand read transposed from LDS (ds_read_b64_tr_b16).
+//    Its prologue computes delta = <dout, out> of the lane's column (the two half-waves each
+//    hold half the coordinates) and writes it for the dk/dv and dsink kernels, which run after.
 //  * dk/dv kernel (key-parallel): a workgroup owns 128 keys of one KV head (32 per wave,
 //    their K and V rows held in registers) and walks the 64-query tiles of every query head
 //    of the group that can see them.  S = Q K^T and dP = dO V^T (queries = M, keys = N),
@@ -40,6 +41,9 @@ namespace {
 constexpr int kTK = 128;           // keys per dk/dv workgroup
 #ifndef SWA_BWD_AHEAD
 #define SWA_BWD_AHEAD 8
+#endif
+#ifndef SWA_BWD_AHEAD64
+#define SWA_BWD_AHEAD64 4
 #endif
 
 template <int D>
@@ -143,41 +147,25 @@ __device__ __forceinline__ bf16x8 pack_ks(const f32x16 (&x)[2], int ks) {
 }
 
 // ======================================================================================
-// delta = <dout, out> per (token, head) row, and dsink
+// dsink
 // ======================================================================================
-template <int D>
-__global__ __launch_bounds__(kThreads) void bwd_delta_kernel(DenseBwdParams p) {
-  constexpr int LPR = D / 8;     // lanes per row (16 bytes each)
-  constexpr int RPW = 64 / LPR;  // rows per wave step
-  const int n_rows = p.f.T * p.f.Hq;
-  const int lane = threadIdx.x & 63;
-  const int sub = lane / LPR, u = lane % LPR;
-  const int stride = gridDim.x * (kThreads / 64) * RPW;
-  for (int base = (blockIdx.x * (kThreads / 64) + (int)(threadIdx.x >> 6)) * RPW; base < n_rows; base += stride) {
-    const int r = base + sub;
-    float acc = 0.f;
-    if (r < n_rows) {
-      const int t = r / p.f.Hq, h = r - t * p.f.Hq;
-      const bf16x8 o = *(const bf16x8*)((const __bf16*)p.f.out + (int64_t)t * p.f.o_st + (int64_t)h * p.f.o_sh + 8 * u);
-      const bf16x8 g = *(const bf16x8*)((const __bf16*)p.dout + (int64_t)t * p.do_st + (int64_t)h * p.do_sh + 8 * u);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc = __builtin_fmaf((float)o[e], (float)g[e], acc);
-    }
-#pragma unroll
-    for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, LPR);
-    if (r < n_rows && u == 0) p.delta[r] = acc;
-  }
-}
-
 // dsink_h = -sum_t exp(sink_h - lse[t, h]) delta[t, h]; rows with lse = -inf (padding) add 0.
 __global__ __launch_bounds__(kThreads) void bwd_dsink_kernel(DenseBwdParams p) {
   __shared__ float part[kThreads / 64];
   const int h = blockIdx.x;
   const float s = p.f.sinks[h];
   float acc = 0.f;
-  for (int t = threadIdx.x; t < p.f.T; t += kThreads) {
-    const float l = p.f.lse[(int64_t)t * p.f.Hq + h];
-    if (l != -INFINITY) acc += __expf(s - l) * p.delta[(int64_t)t * p.f.Hq + h];
+  constexpr int kU8 = 8;  // independent loads in flight per thread (the reads are strided by Hq)
+  for (int t0 = threadIdx.x; t0 < p.f.T; t0 += kThreads * kU8) {
+    float l[kU8], d[kU8];
+#pragma unroll
+    for (int u = 0; u < kU8; ++u) {
+      const int t = t0 + u * kThreads;
+      l[u] = t < p.f.T ? p.f.lse[(int64_t)t * p.f.Hq + h] : -INFINITY;
+      d[u] = t < p.f.T ? p.delta[(int64_t)t * p.f.Hq + h] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < kU8; ++u) acc += l[u] != -INFINITY ? __expf(s - l[u]) * d[u] : 0.f;
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
@@ -211,6 +199,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(DenseBwdParams p) {
       const int row = idx / B::U, cu = idx - row * B::U;
       const int t = w.t0 + row / w.HB, h = w.h0 + row % w.HB;
       *(u32x4*)((__bf16*)p.dq + (int64_t)t * p.dq_st + (int64_t)h * p.dq_sh + cu * 8) = u32x4{0, 0, 0, 0};
+      if (cu == 0) p.delta[(int64_t)t * f.Hq + h] = 0.f;
     }
     return;
   }
@@ -226,8 +215,19 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(DenseBwdParams p) {
       gf[s] = *(const bf16x8*)(gb + 16 * s);
     }
   }
+  float dl = 0.f;  // delta = <dout, out> of this column: half the coordinates per half-wave
+  {
+    const __bf16* ob = (const __bf16*)f.out + (int64_t)tq * f.o_st + (int64_t)c.hq * f.o_sh + 8 * c.h2;
+#pragma unroll
+    for (int s = 0; s < B::QF; ++s) {
+      const bf16x8 o8 = *(const bf16x8*)(ob + 16 * s);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dl = __builtin_fmaf((float)o8[e], (float)gf[s][e], dl);
+    }
+    dl = half_swap_sum(dl);
+    if (c.tq < w.t_end && c.h2 == 0) p.delta[(int64_t)c.tq * f.Hq + c.hq] = dl;
+  }
   const float lse2 = f.lse[(int64_t)tq * f.Hq + c.hq] * kLog2e;
-  const float dl = p.delta[(int64_t)tq * f.Hq + c.hq];
   const float c2 = f.c2;
   const __bf16* kbase = (const __bf16*)f.k + (int64_t)w.g * f.k_sh;
   const __bf16* vbase = (const __bf16*)f.v + (int64_t)w.g * f.v_sh;
@@ -354,7 +354,7 @@ __device__ __forceinline__ void dkdv_tile(const u32x4* qb, const u32x4* ob, cons
   constexpr int NS = B::NS, NV = B::NV, NF = 2 * NS + 2 * NV;
   constexpr int EPS = 32 / NS;  // probabilities per dP slot
   constexpr int DPS = 32 / NV;  // dS elements per dV slot
-  constexpr int kAhead = SWA_BWD_AHEAD;
+  constexpr int kAhead = D == 64 ? SWA_BWD_AHEAD64 : SWA_BWD_AHEAD;
   static_assert(32 % NS == 0 && 32 % NV == 0 && NS >= 8, "slot shares");
   bf16x8 frag[NF];
   auto read = [&](int f) {
@@ -370,10 +370,17 @@ __device__ __forceinline__ void dkdv_tile(const u32x4* qb, const u32x4* ob, cons
   bf16x8 pb[4], sb[4];
   __builtin_amdgcn_s_setprio(1);
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): nothing older in flight, later waits count exactly
-  // rows of group x: 32 (x >> 2) + 8 (x & 3) + 4 h2 .. + 3; lse now, delta late in stream 1
-  auto rows = [&](int x) { return 32 * (x >> 2) + 8 * (x & 3) + 4 * h2; };
+  // rows of group j: 32 (j >> 2) + 8 (j & 3) + 4 h2 .. + 3.  Slots are numbered over the four
+  // streams (S, dP, dV, dK); lse group j is used in dP slot 4 j / EPS, delta group j in dV slot
+  // 4 j / DPS, and each is read two slots before its use.
+  auto rows = [&](int j) { return 32 * (j >> 2) + 8 * (j & 3) + 4 * h2; };
+  auto stage_rows = [&](int slot) {
 #pragma unroll
-  for (int x = 0; x < 8; ++x) l4[x] = *(const f32x4*)(lb + rows(x));
+    for (int j = 0; j < 8; ++j) {
+      if (slot == NS + 4 * j / EPS - 2) l4[j] = *(const f32x4*)(lb + rows(j));
+      if (slot == 2 * NS + 4 * j / DPS - 2) d4[j] = *(const f32x4*)(db + rows(j));
+    }
+  };
 #pragma unroll
   for (int f = 0; f < kAhead; ++f) read(f);
   __builtin_amdgcn_sched_barrier(0);
@@ -383,6 +390,7 @@ __device__ __forceinline__ void dkdv_tile(const u32x4* qb, const u32x4* ob, cons
   for (int i = 0; i < NS; ++i) {
     sc[i & 1] = mfma_bf16_32x32x16(frag[i], kf[i >> 1], sc[i & 1]);
     read(i + kAhead);
+    stage_rows(i);
     __builtin_amdgcn_sched_barrier(0);
   }
   // stream 1b: dP (NS MFMAs) with the probabilities of S, EPS per slot
@@ -403,7 +411,7 @@ __device__ __forceinline__ void dkdv_tile(const u32x4* qb, const u32x4* ob, cons
       asm volatile("" : "+v"(sc[bb][a]));  // this slot's probabilities stay in this slot
       if ((x & 7) == 7) pb[x >> 3] = pack_ks(sc, x >> 3);
     }
-    if (i >= NS - 8) d4[i - (NS - 8)] = *(const f32x4*)(db + rows(i - (NS - 8)));
+    stage_rows(NS + i);
     __builtin_amdgcn_sched_barrier(0);
   }
   // stream 2a: dV^T += dO^T P (NV MFMAs) with dS, DPS elements per slot
@@ -419,6 +427,7 @@ __device__ __forceinline__ void dkdv_tile(const u32x4* qb, const u32x4* ob, cons
       asm volatile("" : "+v"(dp[bb][a]));
       if ((x & 7) == 7) sb[x >> 3] = pack_ks(dp, x >> 3);
     }
+    stage_rows(2 * NS + i);
     __builtin_amdgcn_sched_barrier(0);
   }
   // stream 2b: dK^T += Q^T dS (NV MFMAs)
@@ -432,7 +441,7 @@ __device__ __forceinline__ void dkdv_tile(const u32x4* qb, const u32x4* ob, cons
 }
 
 template <int D>
-__global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(DenseBwdParams p) {
+__global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void bwd_dkdv_kernel(DenseBwdParams p) {
   using B = Bw<D>;
   __shared__ u32x4 q0[B::TileUnits];
   __shared__ u32x4 q1[B::TileUnits];
@@ -558,15 +567,11 @@ void dense_bwd_plan(DenseBwdParams& p) {
 namespace {
 template <int D>
 hipError_t bwd_launch(const DenseBwdParams& p, hipStream_t stream) {
-  const int64_t rows = (int64_t)p.f.T * p.f.Hq;
-  const int64_t rows_per_block = (kThreads / 64) * (64 / (D / 8));
-  int64_t gd = (rows + rows_per_block - 1) / rows_per_block;
-  gd = gd > 8192 ? 8192 : gd;
-  hipLaunchKernelGGL(bwd_delta_kernel<D>, dim3((unsigned)gd), dim3(kThreads), 0, stream, p);
-  if (p.f.sinks != nullptr && p.dsinks != nullptr)
-    hipLaunchKernelGGL(bwd_dsink_kernel, dim3((unsigned)p.f.Hq), dim3(kThreads), 0, stream, p);
+  // dq writes delta; the dsink and dk/dv kernels read it after it on the same stream
   const int64_t gq = dense_fwd_grid(p.f);
   if (gq > 0) hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3((unsigned)gq), dim3(kThreads), 0, stream, p);
+  if (p.f.sinks != nullptr && p.dsinks != nullptr)
+    hipLaunchKernelGGL(bwd_dsink_kernel, dim3((unsigned)p.f.Hq), dim3(kThreads), 0, stream, p);
   const int64_t gk = ((int64_t)p.kv_n_work + kXcds - 1) / kXcds * kXcds;
   if (gk > 0) hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3((unsigned)gk), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
