@@ -130,7 +130,7 @@ int32_t varlen_attn_fwd(const swa_tensor* q, const swa_tensor* k, const swa_tens
  * sinks), its output out and log-sum-exp lse, and dout = dL/dout, for every allowed
  * pair (i, j) of a document and query head h (KV head g):
  *     P_ij   = exp(scale <q[i,h,:], k[j,g,:]> - lse[i,h])
- *     delta  = <dout[i,h,:], out[i,h,:]>                        (written to delta[i,h])
+ *     delta  = <dout[i,h,:], out[i,h,:]>
  *     dS_ij  = P_ij (<dout[i,h,:], v[j,g,:]> - delta[i,h])
  *     dq[i,h,:] = scale sum_j dS_ij k[j,g,:]
  *     dk[j,g,:] = scale sum_{i, h of group g} dS_ij q[i,h,:]
@@ -145,10 +145,10 @@ int32_t varlen_attn_fwd(const swa_tensor* q, const swa_tensor* k, const swa_tens
  *   cu_seqlens, n_docs, window, scale, sinks  as for varlen_attn_fwd
  *   dsinks             device f32 [Hq], required when sinks is given (written), else
  *                      ignored
- *   delta              device f32 [T, Hq] contiguous, written (a workspace the caller
- *                      owns: the library allocates nothing)
- *   stream             hipStream_t; dq (which also writes delta), dsink (with sinks) and
- *                      dk/dv kernels are enqueued in that order
+ *   delta              device f32 [T, Hq] contiguous workspace the caller owns (the
+ *                      library allocates nothing); its contents on return are unspecified
+ *   stream             hipStream_t; the dq (which also computes delta), dk/dv and, with
+ *                      sinks, two dsink reduction kernels are enqueued in that order
  * Supported: D in {64, 128}, T * Hq < 2^30. Errors: as varlen_attn_fwd; SWA_ERR_NULL when lse,
  * delta or (with sinks) dsinks is NULL; SWA_ERR_ARG when a gradient aliases an input or
  * another gradient. Arithmetic: bf16 matrix products (P and dS rounded to bf16 as

@@ -153,7 +153,7 @@ def varlen_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torc
     """Backward of varlen_attn_fwd (bf16, head_dim 64 or 128) from its out and lse.
 
     Returns (dq, dk, dv, dsinks) — dsinks is None without sinks.  ``delta`` is a
-    [T, Hq] fp32 workspace (allocated here when not given).
+    [T, Hq] fp32 workspace (allocated here when not given; contents unspecified on return).
     """
     lib = load_library()
     T, Hq, D = q.shape

@@ -11,7 +11,7 @@
 //   dsink_h = -sum_i exp(sink_h - lse_i) delta_i
 //
 // Design (MFMA 32x32x16 bf16, fp32 accumulation, no atomics, no scratch beyond `delta`):
-//  * dsink kernel: one workgroup per head reduces over the tokens in a fixed order.
+//  * dsink: two deterministic reduction passes (per 256-token chunk across heads, then per head).
 //  * dq kernel (query-parallel): the forward's workgroup decomposition (per document, 128
 //    query columns = tokens x folded GQA heads, XCD-aware placement).  Per 64-key tile:
 //    S^T = K Q^T and dP^T = V dO^T with q and dout of the lane's column in registers, so
@@ -150,23 +150,38 @@ __device__ __forceinline__ bf16x8 pack_ks(const f32x16 (&x)[2], int ks) {
 // dsink
 // ======================================================================================
 // dsink_h = -sum_t exp(sink_h - lse[t, h]) delta[t, h]; rows with lse = -inf (padding) add 0.
-__global__ __launch_bounds__(kThreads) void bwd_dsink_kernel(DenseBwdParams p) {
+// Two deterministic passes after the dk/dv kernel (which is the last reader of delta):
+// one workgroup per 256-token chunk reads the chunk's rows across the heads (coalesced) and
+// leaves each head's partial sum in the chunk's first delta row; one workgroup per head then
+// adds the chunk partials in a fixed order.
+constexpr int kSinkChunk = 256;
+__global__ __launch_bounds__(kThreads) void bwd_dsink_partial_kernel(DenseBwdParams p) {
+  const int Hq = p.f.Hq, T = p.f.T;
+  const int t0 = blockIdx.x * kSinkChunk, t1 = min(t0 + kSinkChunk, T);
+  for (int h = threadIdx.x; h < Hq; h += kThreads) {
+    const float s = p.f.sinks[h];
+    float acc = 0.f;
+    for (int t = t0; t < t1; t += 16) {
+      float l[16], d[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const bool ok = t + u < t1;
+        l[u] = ok ? p.f.lse[(int64_t)(t + u) * Hq + h] : -INFINITY;
+        d[u] = ok ? p.delta[(int64_t)(t + u) * Hq + h] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < 16; ++u) acc += l[u] != -INFINITY ? __expf(s - l[u]) * d[u] : 0.f;
+    }
+    p.delta[(int64_t)t0 * Hq + h] = acc;  // this thread alone read column h of the chunk
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void bwd_dsink_reduce_kernel(DenseBwdParams p) {
   __shared__ float part[kThreads / 64];
   const int h = blockIdx.x;
-  const float s = p.f.sinks[h];
+  const int n_chunks = (p.f.T + kSinkChunk - 1) / kSinkChunk;
   float acc = 0.f;
-  constexpr int kU8 = 8;  // independent loads in flight per thread (the reads are strided by Hq)
-  for (int t0 = threadIdx.x; t0 < p.f.T; t0 += kThreads * kU8) {
-    float l[kU8], d[kU8];
-#pragma unroll
-    for (int u = 0; u < kU8; ++u) {
-      const int t = t0 + u * kThreads;
-      l[u] = t < p.f.T ? p.f.lse[(int64_t)t * p.f.Hq + h] : -INFINITY;
-      d[u] = t < p.f.T ? p.delta[(int64_t)t * p.f.Hq + h] : 0.f;
-    }
-#pragma unroll
-    for (int u = 0; u < kU8; ++u) acc += l[u] != -INFINITY ? __expf(s - l[u]) * d[u] : 0.f;
-  }
+  for (int c = threadIdx.x; c < n_chunks; c += kThreads) acc += p.delta[(int64_t)c * kSinkChunk * p.f.Hq + h];
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
   if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = acc;
@@ -567,13 +582,16 @@ void dense_bwd_plan(DenseBwdParams& p) {
 namespace {
 template <int D>
 hipError_t bwd_launch(const DenseBwdParams& p, hipStream_t stream) {
-  // dq writes delta; the dsink and dk/dv kernels read it after it on the same stream
+  // dq writes delta; the dk/dv kernel reads it, then the dsink passes reuse it (same stream)
   const int64_t gq = dense_fwd_grid(p.f);
   if (gq > 0) hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3((unsigned)gq), dim3(kThreads), 0, stream, p);
-  if (p.f.sinks != nullptr && p.dsinks != nullptr)
-    hipLaunchKernelGGL(bwd_dsink_kernel, dim3((unsigned)p.f.Hq), dim3(kThreads), 0, stream, p);
   const int64_t gk = ((int64_t)p.kv_n_work + kXcds - 1) / kXcds * kXcds;
   if (gk > 0) hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3((unsigned)gk), dim3(kThreads), 0, stream, p);
+  if (p.f.sinks != nullptr && p.dsinks != nullptr) {
+    const unsigned n_chunks = (unsigned)((p.f.T + kSinkChunk - 1) / kSinkChunk);
+    hipLaunchKernelGGL(bwd_dsink_partial_kernel, dim3(n_chunks), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL(bwd_dsink_reduce_kernel, dim3((unsigned)p.f.Hq), dim3(kThreads), 0, stream, p);
+  }
   return hipGetLastError();
 }
 }  // namespace
