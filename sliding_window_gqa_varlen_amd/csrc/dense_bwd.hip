@@ -19,7 +19,8 @@
 //    dQ^T += K^T dS^T with the K^T operand read transposed from LDS (ds_read_b64_tr_b16).
 //    Its prologue computes delta = <dout, out> of the lane's column (the two half-waves each
 //    hold half the coordinates) and writes it for the dk/dv and dsink kernels, which run after.
-//  * dk/dv kernel (key-parallel): a workgroup owns 128 keys of one KV head (32 per wave,
+//  * dk/dv kernel (key-parallel): a workgroup owns 128 keys of one KV head (32 per wave with
+//    32x32 MFMAs for head_dim 64, 16 per wave of 8 waves with 16x16x32 MFMAs for head_dim 128;
 //    their K and V rows held in registers) and walks the 64-query tiles of every query head
 //    of the group that can see them.  S = Q K^T and dP = dO V^T (queries = M, keys = N),
 //    so the lane of a key column holds P and dS in the B-operand layout of
@@ -571,6 +572,251 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void bwd_dkdv_kernel(Den
   }
 }
 
+// --------------------------------------------------------------------------------------
+// dk/dv for head_dim 128 with v_mfma_f32_16x16x32_bf16: 8 waves x 16 keys per workgroup.
+// Per wave: 2 x 32 accumulators, 32 registers of K/V rows, 2 x 16 of S/dP, so two waves fit a
+// SIMD (the 32-key variant above needs one SIMD per wave).  16x16x32 operands: A[l % 16][8 (l / 16)
+// + e], B[8 (l / 16) + e][l % 16], C[4 (l / 16) + a][l % 16].  The lane of key column n = l % 16
+// and group g = l / 16 holds S and dP for query rows 16 b + 4 g + a of the 64-query tile (b, a <
+// 4); k-step s of the dV / dK products takes rows 32 s + 4 g + e (e < 4) and 32 s + 16 + 4 g + e - 4
+// (e >= 4), which are exactly the lane's values of blocks 2 s and 2 s + 1, and the matching
+// transposed A operand reads column 16 m + l % 16 of those rows (ds_read_b64_tr_b16: supplier lane
+// j of a 16-lane group gives row R + j / 4, columns 16 m + 4 (j % 4) .. + 3).
+constexpr int kT16 = 512;
+
+// Swizzle of the Q / dO tiles of this kernel: row bits 0-2 to unit bits 1-3, row bit 3 to unit
+// bit 0.  Row reads take one unit of 16 consecutive rows (a bijection of r & 15 keeps them
+// conflict-free); a transposed read pass takes units {2 m, 2 m + 1} of 8 consecutive rows, which
+// the distinct unit bits 1-3 of those rows keep apart.
+__device__ __forceinline__ int rt16_key(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// 64 rows x 128 bf16 (rt_key swizzle) into buf by 8 waves: two 4-row blocks per wave
+__device__ __forceinline__ void dma_rows64_w8(const __bf16* base, int64_t st, int r0, int r_last, u32x4* buf,
+                                              int wave, int lane_in) {
+  const int lane = opaque(lane_in);
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(base + (int64_t)r0 * st), (short)0, -1, kBufferWord3);
+  const uint32_t stb = (uint32_t)st * 2u;
+  const int lim = r_last - r0;
+  const int lr = lane >> 4, lp = lane & 15;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int blk = i * 8 + wave;
+    const int r = blk * 4 + lr;
+    const int cu = lp ^ rt16_key(r);
+    u32x4* dst = buf + __builtin_amdgcn_readfirstlane(blk * 64);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)dst, 16, (uint32_t)min(r, lim) * stb + (uint32_t)cu * 16u,
+                                             0, 0, 0);
+  }
+}
+
+// One 64-query x 16-key tile as fenced streams (S, dP with the probabilities, dV with dS, dK).
+template <bool MASK>
+__device__ __forceinline__ void dkdv16_tile(const u32x4* qb, const u32x4* ob, const float* lb, const float* db,
+                                            const bf16x8 (&kf)[4], const bf16x8 (&vf)[4], int raddr,
+                                            const int (&toff)[8], float c2, f32x4 (&dk)[8], f32x4 (&dv)[8],
+                                            int qoff, int eoff, int W, int g) {
+  constexpr int kAhead = SWA_BWD_AHEAD;
+  bf16x8 frag[64];
+  auto read = [&](int f) {
+    if (f < 32) {  // S (f < 16) or dP: query block b = f & 3, k-step s = (f >> 2) & 3
+      const char* t = (const char*)(f < 16 ? qb : ob);
+      frag[f] = *(const bf16x8*)(t + ((raddr ^ (64 * ((f >> 2) & 3))) + 4096 * (f & 3)));
+    } else {       // dV (f < 48) or dK: output block m = f & 7, k-step s = (f >> 3) & 1
+      const char* t = (const char*)(f < 48 ? ob : qb) + toff[f & 7] + 8192 * ((f >> 3) & 1);
+      const bf16x4 lo4 = lds_read_tr4((const __bf16*)t);
+      const bf16x4 hi4 = lds_read_tr4((const __bf16*)(t + 4096));
+      frag[f] = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+  };
+  f32x4 l4[4], d4[4];  // lse / delta of query rows 16 b + 4 g + (0..3)
+  f32x4 sc[4], dp[4];
+  bf16x8 pb[2], sb[2];
+  // lse block b is used in dP slot 4 b, delta block b in dV slot 4 b; each read two slots before
+  auto stage_rows = [&](int slot) {
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      if (slot == 16 + 4 * b - 2) l4[b] = *(const f32x4*)(lb + 16 * b + 4 * g);
+      if (slot == 32 + 4 * b - 2) d4[b] = *(const f32x4*)(db + 16 * b + 4 * g);
+    }
+  };
+  __builtin_amdgcn_s_setprio(1);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): nothing older in flight, later waits count exactly
+#pragma unroll
+  for (int f = 0; f < kAhead; ++f) read(f);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int b = 0; b < 4; ++b) sc[b] = dp[b] = f32x4{};
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {  // S
+    sc[i & 3] = mfma16(frag[i], kf[i >> 2], sc[i & 3]);
+    read(i + kAhead);
+    stage_rows(i);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {  // dP, with probability i of the lane's 16 in this slot
+    dp[i & 3] = mfma16(frag[16 + i], vf[i >> 2], dp[i & 3]);
+    read(16 + i + kAhead);
+    const int b = i >> 2, a = i & 3;
+    float pr = fast_exp2(__builtin_fmaf(sc[b][a], c2, l4[b][a] * -kLog2e));
+    if constexpr (MASK) {
+      const int d = qoff + 16 * b + 4 * g + a;  // query - key
+      pr = (d >= 0 && d < eoff && (W == 0 || d < W)) ? pr : 0.f;
+    }
+    sc[b][a] = pr;
+    asm volatile("" : "+v"(sc[b][a]));
+    if (i == 7 || i == 15) {
+      const int s = i >> 3;
+      f32x8 pf;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pf[e] = sc[2 * s + (e >> 2)][e & 3];
+      pb[s] = cvt_bf16x8(pf);
+    }
+    stage_rows(16 + i);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {  // dV, with dS element i in this slot
+    dv[i & 7] = mfma16(frag[32 + i], pb[i >> 3], dv[i & 7]);
+    read(32 + i + kAhead);
+    const int b = i >> 2, a = i & 3;
+    dp[b][a] = sc[b][a] * (dp[b][a] - d4[b][a]);
+    asm volatile("" : "+v"(dp[b][a]));
+    if (i == 7 || i == 15) {
+      const int s = i >> 3;
+      f32x8 pf;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pf[e] = dp[2 * s + (e >> 2)][e & 3];
+      sb[s] = cvt_bf16x8(pf);
+    }
+    stage_rows(32 + i);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {  // dK
+    dk[i & 7] = mfma16(frag[48 + i], sb[i >> 3], dk[i & 7]);
+    if (48 + i + kAhead < 64) read(48 + i + kAhead);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  __builtin_amdgcn_s_setprio(0);
+}
+
+__global__ __launch_bounds__(kT16, 1) void bwd_dkdv16_kernel(DenseBwdParams p) {
+  constexpr int U = 16;
+  __shared__ u32x4 q0[64 * U];
+  __shared__ u32x4 q1[64 * U];
+  __shared__ u32x4 o0[64 * U];
+  __shared__ u32x4 o1[64 * U];
+  __shared__ f32x4 lsv[4][16];
+  float* ls0 = (float*)lsv[0];
+  float* ls1 = (float*)lsv[1];
+  float* dl0 = (float*)lsv[2];
+  float* dl1 = (float*)lsv[3];
+  const DenseFwdParams& f = p.f;
+
+  KeyTile w;
+  if (!decode_key_tile(p, w)) return;
+  if (w.padding) {
+    const int n_rows = w.k1 - w.k0;
+    for (int idx = threadIdx.x; idx < n_rows * U; idx += kT16) {
+      const int row = idx / U, cu = idx - row * U;
+      const int64_t t = w.k0 + row;
+      *(u32x4*)((__bf16*)p.dk + t * p.dk_st + (int64_t)w.g * p.dk_sh + cu * 8) = u32x4{0, 0, 0, 0};
+      *(u32x4*)((__bf16*)p.dv + t * p.dv_st + (int64_t)w.g * p.dv_sh + cu * 8) = u32x4{0, 0, 0, 0};
+    }
+    return;
+  }
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int n = lane & 15, g = lane >> 4;
+  const int W = f.window, e_doc = w.seg_end;
+  const int kw0 = w.k0 + 16 * wave;  // this wave's keys kw0 .. kw0 + 15
+  const bool has_keys = kw0 < w.k1;
+  const int key = kw0 + n;
+
+  bf16x8 kf[4], vf[4];  // B operands: K / V row of this lane's key, coordinates 32 s + 8 g .. + 7
+  {
+    const int kr = min(key, w.k1 - 1);
+    const __bf16* kb = (const __bf16*)f.k + (int64_t)kr * f.k_st + (int64_t)w.g * f.k_sh + 8 * g;
+    const __bf16* vb = (const __bf16*)f.v + (int64_t)kr * f.v_st + (int64_t)w.g * f.v_sh + 8 * g;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      kf[s] = *(const bf16x8*)(kb + 32 * s);
+      vf[s] = *(const bf16x8*)(vb + 32 * s);
+    }
+  }
+  f32x4 dk[8], dv[8];
+#pragma unroll
+  for (int m = 0; m < 8; ++m) dk[m] = dv[m] = f32x4{};
+  const int i_hi = W ? min(e_doc, w.k1 - 1 + W) : e_doc;
+  const int n_qt = (i_hi - w.k0 + 63) / 64;
+  const int n_it = f.G * n_qt;
+  // row reads: row 16 b + n, logical unit 4 s + g -> physical (4 s + g) ^ key(n) = (g ^ key(n)) ^ 4 s
+  const int raddr = n * U * 16 + ((g ^ rt16_key(n)) << 4);
+  int toff[8];  // transposed reads: supplier row 4 g + n / 4 (+ 32 s, + 16), columns 16 m + 4 (n % 4)
+  {
+    const int r = 4 * g + (n >> 2);
+    const int key0 = rt16_key(r);  // the same for rows + 16 and + 32 s
+#pragma unroll
+    for (int m = 0; m < 8; ++m) toff[m] = ((r * U + ((2 * m + ((n & 3) >> 1)) ^ key0)) * 8 + (n & 1) * 4) * 2;
+  }
+  const float c2 = f.c2;
+
+  auto issue = [&](int it, u32x4* qb, u32x4* ob, float* lb, float* db) {
+    const int h = w.g * f.G + it / n_qt;
+    const int i0 = w.k0 + 64 * (it % n_qt);
+    dma_rows64_w8((const __bf16*)f.q + (int64_t)h * f.q_sh, f.q_st, i0, i_hi - 1, qb, wave, lane);
+    dma_rows64_w8((const __bf16*)p.dout + (int64_t)h * p.do_sh, p.do_st, i0, i_hi - 1, ob, wave, lane);
+    if (wave == 0) dma_rowvals(f.lse, f.Hq, h, i0, i_hi - 1, lb, lane);
+    if (wave == 1) dma_rowvals(p.delta, f.Hq, h, i0, i_hi - 1, db, lane);
+  };
+  auto step = [&](int it, const u32x4* qb, const u32x4* ob, const float* lb, const float* db) {
+    const int i0 = w.k0 + 64 * (it % n_qt);
+    if (!has_keys || i0 + 63 < kw0 || (W != 0 && i0 > kw0 + 15 + W - 1)) return;
+    const bool need_mask = !(i0 >= kw0 + 15 && i0 + 63 < e_doc && (W == 0 || i0 + 63 - kw0 < W));
+    if (need_mask)
+      dkdv16_tile<true>(qb, ob, lb, db, kf, vf, raddr, toff, c2, dk, dv, i0 - key, e_doc - key, W, g);
+    else
+      dkdv16_tile<false>(qb, ob, lb, db, kf, vf, raddr, toff, c2, dk, dv, i0 - key, e_doc - key, W, g);
+  };
+
+  issue(0, q0, o0, ls0, dl0);
+  int it = 0;
+  for (; it + 1 < n_it; it += 2) {
+    wait_vm0();
+    barrier_keep_loads();
+    issue(it + 1, q1, o1, ls1, dl1);
+    step(it, q0, o0, ls0, dl0);
+    wait_vm0();
+    barrier_keep_loads();
+    if (it + 2 < n_it) issue(it + 2, q0, o0, ls0, dl0);
+    step(it + 1, q1, o1, ls1, dl1);
+  }
+  if (it < n_it) {
+    wait_vm0();
+    barrier_keep_loads();
+    step(it, q0, o0, ls0, dl0);
+  }
+
+  if (has_keys && key < w.k1) {
+    __bf16* kb = (__bf16*)p.dk + (int64_t)key * p.dk_st + (int64_t)w.g * p.dk_sh + 4 * g;
+    __bf16* vb = (__bf16*)p.dv + (int64_t)key * p.dv_st + (int64_t)w.g * p.dv_sh + 4 * g;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      f32x4 rk = dk[m];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) rk[e] *= f.scale;
+      *(bf16x4*)(kb + 16 * m) = cvt_bf16x4(rk);
+      *(bf16x4*)(vb + 16 * m) = cvt_bf16x4(dv[m]);
+    }
+  }
+}
+
 }  // namespace
 
 void dense_bwd_plan(DenseBwdParams& p) {
@@ -586,7 +832,12 @@ hipError_t bwd_launch(const DenseBwdParams& p, hipStream_t stream) {
   const int64_t gq = dense_fwd_grid(p.f);
   if (gq > 0) hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3((unsigned)gq), dim3(kThreads), 0, stream, p);
   const int64_t gk = ((int64_t)p.kv_n_work + kXcds - 1) / kXcds * kXcds;
-  if (gk > 0) hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3((unsigned)gk), dim3(kThreads), 0, stream, p);
+  if (gk > 0) {
+    if (D == 128)
+      hipLaunchKernelGGL(bwd_dkdv16_kernel, dim3((unsigned)gk), dim3(kT16), 0, stream, p);
+    else
+      hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3((unsigned)gk), dim3(kThreads), 0, stream, p);
+  }
   if (p.f.sinks != nullptr && p.dsinks != nullptr) {
     const unsigned n_chunks = (unsigned)((p.f.T + kSinkChunk - 1) / kSinkChunk);
     hipLaunchKernelGGL(bwd_dsink_partial_kernel, dim3(n_chunks), dim3(kThreads), 0, stream, p);
