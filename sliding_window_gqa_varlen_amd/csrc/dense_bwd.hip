@@ -34,6 +34,8 @@
 //    m = (r >> 1) & 7 goes to m ^ ((m & 1) << 2).  V tiles (dq kernel) are only read row-wise.
 //  * Tiles travel HBM -> LDS by buffer_load ... lds into two statically named buffers per
 //    operand (loop unrolled by two): the next tile is in flight while this one is used.
+#include <climits>
+
 #include "dense_common.h"
 
 namespace swa {
@@ -330,16 +332,112 @@ struct KeyTile {
   bool padding;
 };
 
-// blockIdx -> (KV head, 128-key tile of a segment); each KV head's tiles on one XCD, each
+__device__ __forceinline__ int wave_sum(int x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
+  return x;
+}
+
+// Rank r of the head's key tiles, heaviest first, when the segments fit a wave's lanes
+// (n_docs + 2 <= 64).  The query tiles a key tile walks are ceil(min(R, 127 + W) / 64) (R = keys
+// from the tile to the document end; no cap without a window), non-increasing along a document,
+// so the tiles of a document with at least x query tiles are its first
+// min(n_tiles, ceil((len - 64 (x - 1)) / 128)).  A binary search on x over the lane-wise counts
+// finds the weight of rank r; ties go in document order.  Padding segments come last.
+__device__ __forceinline__ bool decode_heavy_first(const DenseFwdParams& f, int r, KeyTile& w) {
+  const int lane = threadIdx.x & 63;
+  const int nseg = f.n_docs + 2;
+  const bool seg_ok = lane < nseg;
+  const int st = seg_ok ? seg_bound(f, lane) : 0;
+  const int en = seg_ok ? seg_bound(f, lane + 1) : 0;
+  const int len = en - st;
+  const int nt = (len + kTK - 1) / kTK;
+  const bool real = seg_ok && lane >= 1 && lane <= f.n_docs;
+  const int cap = f.window ? 127 + f.window : INT_MAX;
+  auto count_ge = [&](int x) -> int {
+    const int need = 64 * (x - 1);
+    if (!real || cap <= need || len <= need) return 0;
+    return min(nt, (len - need + kTK - 1) / kTK);
+  };
+  const int n_real = __builtin_amdgcn_readfirstlane(wave_sum(real ? nt : 0));
+  int seg, t;
+  if (r < n_real) {
+    int lo = 1, hi = f.T / 64 + 2;  // count_ge(lo) > r >= count_ge(hi) = 0
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (__builtin_amdgcn_readfirstlane(wave_sum(count_ge(mid))) > r) lo = mid; else hi = mid;
+    }
+    const int above = count_ge(lo + 1);
+    const int j = r - __builtin_amdgcn_readfirstlane(wave_sum(above));  // rank among tiles of weight lo
+    const int eq = count_ge(lo) - above;
+    int incl = eq;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off);
+      if (lane >= off) incl += y;
+    }
+    const bool mine = eq > 0 && j >= incl - eq && j < incl;
+    const uint64_t owner = __builtin_amdgcn_ballot_w64(mine);
+    if (owner == 0) return false;  // unreachable: rank r always has an owner
+    seg = __builtin_amdgcn_readfirstlane(__builtin_ctzll(owner));
+    t = __builtin_amdgcn_readlane(above, seg) + (j - (__builtin_amdgcn_readlane(incl, seg) -
+                                                      __builtin_amdgcn_readlane(eq, seg)));
+    w.padding = false;
+  } else {
+    const int rp = r - n_real;
+    const int nt0 = __builtin_amdgcn_readlane(nt, 0), ntn = __builtin_amdgcn_readlane(nt, nseg - 1);
+    if (rp < nt0) {
+      seg = 0;
+      t = rp;
+    } else if (rp - nt0 < ntn) {
+      seg = nseg - 1;
+      t = rp - nt0;
+    } else {
+      return false;
+    }
+    w.padding = true;
+  }
+  w.seg_start = __builtin_amdgcn_readlane(st, seg);
+  w.seg_end = __builtin_amdgcn_readlane(en, seg);
+  w.k0 = w.seg_start + t * kTK;
+  w.k1 = min(w.k0 + kTK, w.seg_end);
+  return true;
+}
+
+// blockIdx -> (KV head, 128-key tile of a segment); each KV head's tiles on one XCD, heaviest
+// first (the tail of a launch is then made of light tiles).  With more than 62 documents: each
 // document's tiles first-first (under a causal mask the first keys are seen by the most queries).
+// Workgroups reach the XCDs round-robin (x = blockIdx % 8, j = blockIdx / 8 is the order within
+// an XCD).  A KV head's tiles stay on the XCDs that hold its K/V in L2.  In heavy-first order
+// (full causal): with Hkv a multiple of 8 each XCD owns whole heads; with Hkv dividing 8 the
+// 8 / Hkv XCDs of a head deal its ranks round robin (so each gets the same mix of heavy and light
+// tiles).  Otherwise contiguous ranges (consecutive tiles of a document share an L2, which is
+// what windowed problems, whose tiles weigh about the same, gain most from).
+__device__ __forceinline__ bool key_tile_slot(const DenseBwdParams& p, int& g, int& r) {
+  const int Hkv = p.f.Hkv, VT = p.kv_n_vtiles;
+  const int x = blockIdx.x % kXcds, j = blockIdx.x / kXcds;
+  if (p.kv_heavy_first && Hkv % kXcds == 0) {
+    g = x + kXcds * (j / VT);
+    r = j % VT;
+    return g < Hkv;
+  }
+  if (p.kv_heavy_first && kXcds % Hkv == 0) {
+    const int m = kXcds / Hkv;
+    g = x % Hkv;
+    r = j * m + x / Hkv;
+    return r < VT;
+  }
+  const int L = x * (gridDim.x / kXcds) + j;
+  g = L / VT;
+  r = L - g * VT;
+  return L < p.kv_n_work;
+}
+
 __device__ __forceinline__ bool decode_key_tile(const DenseBwdParams& p, KeyTile& w) {
   const DenseFwdParams& f = p.f;
-  const int per_xcd = gridDim.x / kXcds;
-  const int L = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
-  if (L >= p.kv_n_work) return false;
-  const int VT = p.kv_n_vtiles;
-  w.g = L / VT;
-  const int v = L - w.g * VT;
+  int v;
+  if (!key_tile_slot(p, w.g, v)) return false;
+  if (p.kv_heavy_first) return decode_heavy_first(f, v, w);
   int lo = 0, hi = f.n_docs + 2;
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
@@ -823,6 +921,9 @@ void dense_bwd_plan(DenseBwdParams& p) {
   dense_fwd_plan(p.f);
   p.kv_n_vtiles = p.f.T / kTK + p.f.n_docs + 2;
   p.kv_n_work = p.f.Hkv * p.kv_n_vtiles;
+  // heavy-first key tiles where the causal mask makes their weights uneven (segments must fit
+  // the lanes of one wave)
+  p.kv_heavy_first = p.f.window == 0 && p.f.n_docs + 2 <= 64 ? 1 : 0;
 }
 
 namespace {
@@ -831,9 +932,14 @@ hipError_t bwd_launch(const DenseBwdParams& p, hipStream_t stream) {
   // dq writes delta; the dk/dv kernel reads it, then the dsink passes reuse it (same stream)
   const int64_t gq = dense_fwd_grid(p.f);
   if (gq > 0) hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3((unsigned)gq), dim3(kThreads), 0, stream, p);
-  const int64_t gk = ((int64_t)p.kv_n_work + kXcds - 1) / kXcds * kXcds;
+  // grid of key_tile_slot: 8 XCD columns of (Hkv / 8) VT, ceil(VT / (8 / Hkv)) or ceil(Hkv VT / 8) slots
+  const int64_t Hkv = p.f.Hkv, VT = p.kv_n_vtiles;
+  const int64_t per_xcd = p.kv_heavy_first && Hkv % kXcds == 0 ? Hkv / kXcds * VT
+                          : p.kv_heavy_first && kXcds % Hkv == 0 ? (VT + kXcds / Hkv - 1) / (kXcds / Hkv)
+                                                                 : (Hkv * VT + kXcds - 1) / kXcds;
+  const int64_t gk = per_xcd * kXcds;
   if (gk > 0) {
-    if (D == 128)
+    if constexpr (D == 128)
       hipLaunchKernelGGL(bwd_dkdv16_kernel, dim3((unsigned)gk), dim3(kT16), 0, stream, p);
     else
       hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3((unsigned)gk), dim3(kThreads), 0, stream, p);

@@ -53,6 +53,7 @@ struct DenseBwdParams {
   float* dsinks;        // [Hq] or null (written when f.sinks is set)
   int32_t kv_n_vtiles;  // virtual 128-key tiles per KV head
   int32_t kv_n_work;    // Hkv * kv_n_vtiles
+  int32_t kv_heavy_first;  // key tiles in heavy-first order (set by dense_bwd_plan)
 };
 
 // Fills the key-tile plan (and, through dense_fwd_plan, the query-tile plan) of p.
