@@ -151,11 +151,10 @@ __device__ __forceinline__ void softmax_tile(f32x16 (&sc)[2], bool need_mask, in
   st.l = st.l * t.alpha + tile_exp(sc, c2, t.mu);
 }
 
-// Half-wave sums combined, sink folded in, one normalisation, one rounding, LSE.
+// Half-wave sums combined, sink folded in; stores the LSE and returns the normaliser.
 // `st.l` holds this half-wave's share of the row sum, or the whole sum if `full_sum`.
-template <typename T, int DB>
-__device__ __forceinline__ void epilogue(const DenseFwdParams& p, const Tile& w, const Cols& c,
-                                         const Softmax& st, const f32x16 (&o)[DB], bool full_sum = false) {
+__device__ __forceinline__ float epilogue_scalars(const DenseFwdParams& p, const Tile& w, const Cols& c,
+                                                  const Softmax& st, bool full_sum) {
   const float lt = full_sum ? st.l : half_swap_sum(st.l);
   const float m2 = st.mref;  // reference max in log2 units (-inf if nothing was visible)
   float inv, lse_v;
@@ -170,6 +169,15 @@ __device__ __forceinline__ void epilogue(const DenseFwdParams& p, const Tile& w,
     inv = 1.f / lt;
     lse_v = (m2 + __builtin_amdgcn_logf(lt)) * kLn2;
   }
+  if (p.lse != nullptr && c.h2 == 0 && c.tq < w.t_end) p.lse[(int64_t)c.tq * p.Hq + c.hq] = lse_v;
+  return inv;
+}
+
+// One normalisation, one rounding, stores straight from the accumulator layout.
+template <typename T, int DB>
+__device__ __forceinline__ void epilogue(const DenseFwdParams& p, const Tile& w, const Cols& c,
+                                         const Softmax& st, const f32x16 (&o)[DB], bool full_sum = false) {
+  const float inv = epilogue_scalars(p, w, c, st, full_sum);
   if (c.tq < w.t_end) {
     T* ob = (T*)p.out + (int64_t)c.tq * p.o_st + (int64_t)c.hq * p.o_sh;
 #pragma unroll
@@ -183,7 +191,44 @@ __device__ __forceinline__ void epilogue(const DenseFwdParams& p, const Tile& w,
         if constexpr (std::is_same<T, __bf16>::value) *(bf16x4*)dst = cvt_bf16x4(r);
         else *(f32x4*)dst = r;
       }
-    if (p.lse != nullptr && c.h2 == 0) p.lse[(int64_t)c.tq * p.Hq + c.hq] = lse_v;
+  }
+}
+
+// bf16 output of one wave through LDS.  The wave's 32 query columns are 32 rows of D
+// values; lane (n, h2) holds dims 32 d + 8 i + 4 h2 + (0..3) of column n.  Each lane writes
+// its bf16 quads into a wave-private image (column n at n * 2D bytes, 16-byte unit u at
+// u ^ key(n) so a half-wave's writes spread over the banks), then reads it back 16 bytes per
+// lane: one store instruction writes 64 consecutive units = whole rows of 512 / D adjacent
+// columns, and columns with adjacent heads of one token are adjacent in memory.  Direct
+// stores from the accumulator layout would touch 32 rows with 8 bytes each per instruction.
+template <int D>
+__device__ __forceinline__ int out_key(int n) {
+  if constexpr (D == 64) return (n >> 1) & 7;
+  else return n & 15;
+}
+template <int D>
+__device__ __forceinline__ void store_out_bf16(const DenseFwdParams& p, const Tile& w, const Cols& c, float inv,
+                                               const f32x16 (&o)[D / 32], char* img) {
+  constexpr int U = D / 8;           // 16-byte units per column
+  constexpr int kCols = 512 / D;     // columns per store instruction
+#pragma unroll
+  for (int d = 0; d < D / 32; ++d)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f32x4 r;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) r[e] = o[d][4 * i + e] * inv;
+      *(bf16x4*)(img + c.n * (2 * D) + (((4 * d + i) ^ out_key<D>(c.n)) << 4) + 8 * c.h2) = cvt_bf16x4(r);
+    }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's own writes, in order
+  const int u = c.lane % U;
+#pragma unroll
+  for (int k = 0; k < 32 / kCols; ++k) {
+    const int n = k * kCols + c.lane / U;
+    const u32x4 val = *(const u32x4*)(img + n * (2 * D) + ((u ^ out_key<D>(n)) << 4));
+    const int t = c.tw0 + (n >> p.hb_shift);
+    if (t <= c.tw1)
+      *(u32x4*)((__bf16*)p.out + (int64_t)t * p.o_st + (int64_t)(w.h0 + (n & (w.HB - 1))) * p.o_sh + 8 * u) = val;
   }
 }
 
@@ -493,7 +538,11 @@ __global__ __launch_bounds__(kThreads, D == 64 ? SWA_OCC64 : D == 128 ? 2 : 1) v
   if ((nt - 1) & 1) pv_tile<D>(v1, sc, vo, o, lacc);
   else pv_tile<D>(v0, sc, vo, o, lacc);
   if constexpr (B::kMfmaRowSum) st.l = lacc[0];
-  epilogue<__bf16, B::kDBlocks>(p, w, c, st, o, B::kMfmaRowSum);
+  // every wave is past its last K read (the barrier above): the K buffers hold the output
+  // images, two waves per buffer
+  char* img = (char*)(c.wave < 2 ? k0 : k1) + (c.wave & 1) * (64 * D);
+  const float inv = epilogue_scalars(p, w, c, st, B::kMfmaRowSum);
+  store_out_bf16<D>(p, w, c, inv, o, img);
 }
 
 // ======================================================================================
