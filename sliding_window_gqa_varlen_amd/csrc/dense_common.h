@@ -17,6 +17,12 @@ typedef __attribute__((address_space(3))) void lds_void;
 constexpr int kBufferWord3 = 0x00020000;  // buffer descriptor word 3: 32-bit data format, raw access
 // s_waitcnt vmcnt(0) with expcnt / lgkmcnt unconstrained
 __device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8)); }
+// s_waitcnt vmcnt(N) with expcnt / lgkmcnt unconstrained (vector loads complete in order)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
 // workgroup barrier that does not drain outstanding vector-memory loads
 __device__ __forceinline__ void barrier_keep_loads() {
   asm volatile("" ::: "memory");
@@ -54,15 +60,31 @@ __device__ __forceinline__ bool decode_tile(const DenseFwdParams& p, Tile& w) {
   w.g = hc / p.n_chunks;
   const int chunk = hc - w.g * p.n_chunks;
   const int TQ = p.tile_tokens;
-  // segment s holding virtual tile v: A(s) = floor(bound(s) / TQ) + s, A(s) <= v < A(s+1)
-  int lo = 0, hi = p.n_docs + 2;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (seg_bound(p, mid) / TQ + mid <= v) lo = mid; else hi = mid;
+  // segment s holding virtual tile v: A(s) = floor(bound(s) / TQ) + s, A(s) <= v < A(s+1).
+  // A is increasing in s, so the segment is the number of s >= 1 with A(s) <= v: with at
+  // most 64 boundaries lane s loads bound(s) and one ballot counts them (one memory round
+  // trip); otherwise a binary search.
+  int lo, seg_start, seg_end;
+  if (p.n_docs + 3 <= 64) {  // lanes 0 .. n_docs + 2 hold every boundary
+    const int s = threadIdx.x & 63;
+    const int b = seg_bound(p, s);
+    lo = __builtin_amdgcn_readfirstlane(
+        __builtin_popcountll(__builtin_amdgcn_ballot_w64(s >= 1 && s <= p.n_docs + 1 && b < (v - s + 1) * TQ)));
+    seg_start = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_readlane(b, lo));
+    seg_end = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_readlane(b, lo + 1));
+  } else {
+    lo = 0;
+    int hi = p.n_docs + 2;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (seg_bound(p, mid) / TQ + mid <= v) lo = mid; else hi = mid;
+    }
+    seg_start = seg_bound(p, lo);
+    seg_end = seg_bound(p, lo + 1);
   }
   w.seg = lo;
-  w.seg_start = seg_bound(p, lo);
-  const int seg_end = seg_bound(p, lo + 1);
+  w.seg_start = seg_start;
+  if (seg_start / TQ + lo > v) return false;  // only with decreasing cu_seqlens: no tile
   w.t0 = w.seg_start + (v - (w.seg_start / TQ + lo)) * TQ;
   if (w.t0 >= seg_end) return false;
   w.t_end = min(w.t0 + TQ, seg_end);

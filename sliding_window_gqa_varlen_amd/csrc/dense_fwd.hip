@@ -488,12 +488,17 @@ __global__ __launch_bounds__(kThreads, D == 64 ? SWA_OCC64 : D == 128 ? 2 : 1) v
   const int kaddr = c.n * B::U * 16 + ((c.h2 ^ k_key<D>(c.n)) << 4);
   const VOffsets<D> vo = v_offsets<D>(c.lane);
 
-  // prologue: K(0) -> k0; then K(1) -> k1, V(0) -> v0 while S(0) is computed
+  // prologue: K(0) -> k0, V(0) -> v0, K(1) -> k1 all at once; wait for K(0) only (loads
+  // complete in order) while V(0) and K(1) stay in flight through S(0)
   dma_tile<D, false>(kbase, p.k_st, c.k_lo, c.k_hi, k0, c.wave, c.lane);
-  wait_vm0();
-  barrier_keep_loads();
-  if (nt > 1) dma_tile<D, false>(kbase, p.k_st, c.k_lo + kBN, c.k_hi, k1, c.wave, c.lane);
   dma_tile<D, true>(vbase, p.v_st, c.k_lo, c.k_hi, v0, c.wave, c.lane);
+  if (nt > 1) {
+    dma_tile<D, false>(kbase, p.k_st, c.k_lo + kBN, c.k_hi, k1, c.wave, c.lane);
+    wait_vmcnt<2 * B::kDmaPerWave>();
+  } else {
+    wait_vmcnt<B::kDmaPerWave>();
+  }
+  barrier_keep_loads();
   f32x16 sc[2];
   qk_tile<D>(k0, qf, c.n, c.h2, sc);
   if (tile_needs_mask(c, c.k_lo)) mask_tile(sc, c.k_lo, c);
