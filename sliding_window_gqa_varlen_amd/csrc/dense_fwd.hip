@@ -262,34 +262,60 @@ __device__ __forceinline__ int v_key(int r) {
   else return ((r >> 1) & 1) << 2;
 }
 
-// Gather one 64-key tile (rows kb.. clamped to k_hi - 1) of one tensor into `buf` with
-// buffer_load ... lds (MUBUF LDS DMA: the tile base sits in the buffer descriptor, the
-// 64-unit block's row offset in soffset, so a transfer costs a few VALU).  Rows past the
-// tile's last query are clamped to the last valid row (always in bounds); every such key
-// lies after every valid query of the tile, so it is masked and contributes zero.
+// Per-lane voffset of the full-tile transfers: lane row lr = lane / U, unit lp ^ key(row).
+// The row of transfer i is (4 i + wave) R + lr, and every key depends on it only through its
+// low four bits, which take at most two values over i (row steps of 4 R = 16 (D = 128),
+// 32 (D = 64) or 8 (D = 256)): kClasses offsets per lane, computed once per workgroup.
+// D = 256 has no register to spare: it recomputes them per tile (kKeep = false).
 template <int D, bool IS_V>
-__device__ __forceinline__ void dma_tile(const __bf16* base, int64_t st, int kb, int k_hi, u32x4* buf,
-                                         int wave, int lane_in) {
+struct DmaLane {
+  static constexpr bool kKeep = D <= 128;
+  static constexpr int kClasses = (D == 256 && !IS_V) ? 2 : 1;
+  uint32_t off[kClasses];
+};
+template <int D, bool IS_V>
+__device__ __forceinline__ DmaLane<D, IS_V> dma_lane(int64_t st, int lane, int wave) {
   using B = Bf<D>;
   constexpr int R = 64 / B::U;  // rows per 64-unit block
-  const int lane = opaque(lane_in);  // recomputed plan, nothing kept live across the loop
+  const uint32_t stb = (uint32_t)st * 2u;
+  const int lr = lane / B::U, lp = lane % B::U;
+  DmaLane<D, IS_V> d;
+#pragma unroll
+  for (int i = 0; i < DmaLane<D, IS_V>::kClasses; ++i) {
+    const int r = (i * 4 + wave) * R + lr;
+    const int cu = lp ^ (IS_V ? v_key<D>(r) : k_key<D>(r));
+    d.off[i] = (uint32_t)lr * stb + (uint32_t)cu * 16u;
+  }
+  return d;
+}
+
+// Gather one 64-key tile (rows kb.. clamped to k_hi - 1) of one tensor into `buf` with
+// buffer_load ... lds (MUBUF LDS DMA: the tile base sits in the buffer descriptor, the
+// 64-unit block's row offset in soffset and the lane's offset in a register kept across
+// the loop, so a full-tile transfer costs no VALU).  Rows past the tile's last query are
+// clamped to the last valid row (always in bounds); every such key lies after every valid
+// query of the tile, so it is masked and contributes zero.
+template <int D, bool IS_V>
+__device__ __forceinline__ void dma_tile(const __bf16* base, int64_t st, int kb, int k_hi, u32x4* buf,
+                                         int wave, int lane_in, const DmaLane<D, IS_V>& dl) {
+  using B = Bf<D>;
+  constexpr int R = 64 / B::U;  // rows per 64-unit block
   const __amdgpu_buffer_rsrc_t rsrc =
       __builtin_amdgcn_make_buffer_rsrc((void*)(base + (int64_t)kb * st), (short)0, -1, kBufferWord3);
   const uint32_t stb = (uint32_t)st * 2u;  // row stride in bytes (< 2^25)
   const int lim = k_hi - 1 - kb;
-  const int lr = lane / B::U, lp = lane % B::U;
   if (lim >= kBN - 1) {
-    const uint32_t lane_off = (uint32_t)lr * stb;
+    const DmaLane<D, IS_V> d = DmaLane<D, IS_V>::kKeep ? dl : dma_lane<D, IS_V>(st, opaque(lane_in), wave);
 #pragma unroll
     for (int i = 0; i < B::kDmaPerWave; ++i) {
       const int blk = i * 4 + wave;  // wave-uniform 64-unit block
-      const int r = blk * R + lr;
-      const int cu = lp ^ (IS_V ? v_key<D>(r) : k_key<D>(r));
       u32x4* dst = buf + __builtin_amdgcn_readfirstlane(blk * 64);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)dst, 16, lane_off + (uint32_t)cu * 16u,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)dst, 16, d.off[i % DmaLane<D, IS_V>::kClasses],
                                                __builtin_amdgcn_readfirstlane((uint32_t)(blk * R) * stb), 0, 0);
     }
   } else {
+    const int lane = opaque(lane_in);  // the last tile only: recomputed, nothing kept live
+    const int lr = lane / B::U, lp = lane % B::U;
 #pragma unroll
     for (int i = 0; i < B::kDmaPerWave; ++i) {
       const int blk = i * 4 + wave;
@@ -490,10 +516,12 @@ __global__ __launch_bounds__(kThreads, D == 64 ? SWA_OCC64 : D == 128 ? 2 : 1) v
 
   // prologue: K(0) -> k0, V(0) -> v0, K(1) -> k1 all at once; wait for K(0) only (loads
   // complete in order) while V(0) and K(1) stay in flight through S(0)
-  dma_tile<D, false>(kbase, p.k_st, c.k_lo, c.k_hi, k0, c.wave, c.lane);
-  dma_tile<D, true>(vbase, p.v_st, c.k_lo, c.k_hi, v0, c.wave, c.lane);
+  const DmaLane<D, false> kdl = dma_lane<D, false>(p.k_st, c.lane, c.wave);
+  const DmaLane<D, true> vdl = dma_lane<D, true>(p.v_st, c.lane, c.wave);
+  dma_tile<D, false>(kbase, p.k_st, c.k_lo, c.k_hi, k0, c.wave, c.lane, kdl);
+  dma_tile<D, true>(vbase, p.v_st, c.k_lo, c.k_hi, v0, c.wave, c.lane, vdl);
   if (nt > 1) {
-    dma_tile<D, false>(kbase, p.k_st, c.k_lo + kBN, c.k_hi, k1, c.wave, c.lane);
+    dma_tile<D, false>(kbase, p.k_st, c.k_lo + kBN, c.k_hi, k1, c.wave, c.lane, kdl);
     wait_vmcnt<2 * B::kDmaPerWave>();
   } else {
     wait_vmcnt<B::kDmaPerWave>();
@@ -514,8 +542,8 @@ __global__ __launch_bounds__(kThreads, D == 64 ? SWA_OCC64 : D == 128 ? 2 : 1) v
     const int kb = c.k_lo + j * kBN;
     wait_vm0();
     barrier_keep_loads();  // K(j), V(j-1) landed for every wave; K(j-1), V(j-2) consumed
-    if (j + 1 < nt) dma_tile<D, false>(kbase, p.k_st, kb + kBN, c.k_hi, knext, c.wave, c.lane);
-    dma_tile<D, true>(vbase, p.v_st, kb, c.k_hi, vcur_dst, c.wave, c.lane);
+    if (j + 1 < nt) dma_tile<D, false>(kbase, p.k_st, kb + kBN, c.k_hi, knext, c.wave, c.lane, kdl);
+    dma_tile<D, true>(vbase, p.v_st, kb, c.k_hi, vcur_dst, c.wave, c.lane, vdl);
     rescale_o<B::kDBlocks>(ts.move, ts.alpha, o, lacc);
     f32x16 sn[2];
     float sn_max;
