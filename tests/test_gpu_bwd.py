@@ -188,6 +188,22 @@ def test_zero_length_documents_head_and_tail_padding(gpu):
         assert np.all(g[:9] == 0) and np.all(g[120:] == 0)
 
 
+@pytest.mark.parametrize("n_docs,window", [(61, 0), (62, 0), (63, 0), (90, 0), (90, 29)])
+def test_many_documents(gpu, n_docs, window):
+    """Segment decodes on both sides of 61 documents (dq), heaviest-first dk/dv key tiles up to
+    62 documents and document order beyond (causal), with empty documents and padding."""
+    rng = np.random.default_rng(n_docs + window)
+    lengths = [int(x) for x in rng.integers(0, 40, n_docs)]
+    lengths[5] = 0
+    inp = custom(lengths, T=sum(lengths) + 11, Hq=8, Hkv=2, window=window, sinks=window > 0, seed=n_docs, D=128)
+    do = dout_for(inp, n_docs)
+    got = run_bwd(inp, do)
+    check_all(got, oracle_bwd(inp, do), inp, do)
+    T0 = sum(lengths)
+    for g in got[:3]:
+        assert np.all(g[T0:] == 0)
+
+
 def test_packed_documents_elementwise(gpu):
     """2048 tokens in documents of 128..512 tokens, 16 query / 4 KV heads, full causal."""
     w = W.DenseWorkload("bwd", "bf16", T=2048, Hq=16, Hkv=4, D=128, window=0, scale=1.0 / math.sqrt(128.0),

@@ -175,6 +175,23 @@ def test_no_documents_means_all_padding(gpu):
     assert torch.all(out == 0) and torch.all(torch.isneginf(lse))
 
 
+@pytest.mark.parametrize("n_docs", [61, 62, 90])
+@pytest.mark.parametrize("D,window", [(128, 0), (64, 37)])
+def test_many_documents_both_segment_decodes(gpu, n_docs, D, window):
+    """Up to 61 documents the tile decode counts boundaries with one ballot, beyond that it
+    binary-searches cu_seqlens; both, with empty documents and head and tail padding."""
+    rng = np.random.default_rng(n_docs + D)
+    lengths = [int(x) for x in rng.integers(0, 48, n_docs)]
+    lengths[3] = lengths[n_docs // 2] = 0
+    inp = custom(lengths, T=sum(lengths) + 20, Hq=8, Hkv=2, D=D, window=window, dtype="bf16",
+                 sinks=window > 0, seed=n_docs)
+    inp["cu_seqlens"] = inp["cu_seqlens"] + 7  # tokens 0..6 sit before the first document
+    ref_o, ref_l = oracle_full(inp)
+    out, lse = run_dense(inp, "bf16")
+    assert_dense_parity("bf16", out, lse, ref_o, ref_l)
+    assert np.all(out[:7] == 0) and np.all(np.isneginf(lse[:7]))
+
+
 def test_single_token_documents(gpu):
     inp = custom([1] * 300, T=300, Hq=8, Hkv=8, D=128, window=0, dtype="f32", seed=6)
     out, lse = run_dense(inp, "f32")
