@@ -51,12 +51,27 @@ struct Tile {
 
 // Decodes blockIdx into a tile; returns false for idle blocks.
 __device__ __forceinline__ bool decode_tile(const DenseFwdParams& p, Tile& w) {
-  const int per_xcd = gridDim.x / kXcds;
-  const int L = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;  // XCD-aware remap
-  if (L >= p.n_work) return false;
+  // XCD-aware remap: workgroups reach the XCDs round-robin (x = blockIdx % 8, j = blockIdx / 8
+  // is the order within an XCD) and a head chunk's tiles stay on the XCDs whose L2 holds its
+  // K/V.  Under a full causal mask, when 8 / n_hc XCDs share a head chunk they deal its tiles
+  // round robin, so each gets the same mix of heavy and light tiles; otherwise (and for
+  // windows, whose tiles weigh about the same) each XCD takes a contiguous range.
   const int VT = p.n_vtiles;
-  const int hc = L / VT;
-  const int v = VT - 1 - (L - hc * VT);  // each document's tiles last-first
+  const int n_hc = p.Hkv * p.n_chunks;
+  const int x = blockIdx.x % kXcds, j = blockIdx.x / kXcds;
+  int hc, r;
+  if (p.window == 0 && n_hc < kXcds && kXcds % n_hc == 0) {
+    const int m = kXcds / n_hc;
+    hc = x % n_hc;
+    r = j * m + x / n_hc;
+    if (r >= VT) return false;
+  } else {
+    const int L = x * (gridDim.x / kXcds) + j;
+    if (L >= p.n_work) return false;
+    hc = L / VT;
+    r = L - hc * VT;
+  }
+  const int v = VT - 1 - r;  // each document's tiles last-first
   w.g = hc / p.n_chunks;
   const int chunk = hc - w.g * p.n_chunks;
   const int TQ = p.tile_tokens;
