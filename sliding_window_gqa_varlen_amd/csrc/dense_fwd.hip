@@ -55,9 +55,6 @@ constexpr float kRescaleLog2 = 8.f;  // lazy-rescale threshold (log2 units)
 #define SWA_OCC64 3
 #endif
 
-constexpr bf16x8 kOnesBf16x8 = {(__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f,
-                                (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f};
-
 typedef __attribute__((address_space(1))) const void glob_cvoid;
 
 template <typename T, int D>
@@ -132,15 +129,6 @@ __device__ __forceinline__ void rescale_o(bool move, float alpha, f32x16 (&o)[DB
     for (int d = 0; d < DB; ++d) o[d] *= alpha;
   }
 }
-template <int DB>
-__device__ __forceinline__ void rescale_o(bool move, float alpha, f32x16 (&o)[DB], f32x16& lacc) {
-  if (__builtin_amdgcn_ballot_w64(move) != 0) {
-#pragma unroll
-    for (int d = 0; d < DB; ++d) o[d] *= alpha;
-    lacc *= alpha;
-  }
-}
-
 // Full online-softmax step for one tile (used where nothing is interleaved with it).
 template <int DB>
 __device__ __forceinline__ void softmax_tile(f32x16 (&sc)[2], bool need_mask, int kb, const Cols& c, float c2,
@@ -152,10 +140,10 @@ __device__ __forceinline__ void softmax_tile(f32x16 (&sc)[2], bool need_mask, in
 }
 
 // Half-wave sums combined, sink folded in; stores the LSE and returns the normaliser.
-// `st.l` holds this half-wave's share of the row sum, or the whole sum if `full_sum`.
+// `st.l` holds this half-wave's share of the row sum.
 __device__ __forceinline__ float epilogue_scalars(const DenseFwdParams& p, const Tile& w, const Cols& c,
-                                                  const Softmax& st, bool full_sum) {
-  const float lt = full_sum ? st.l : half_swap_sum(st.l);
+                                                  const Softmax& st) {
+  const float lt = half_swap_sum(st.l);
   const float m2 = st.mref;  // reference max in log2 units (-inf if nothing was visible)
   float inv, lse_v;
   if (p.sinks != nullptr) {
@@ -176,8 +164,8 @@ __device__ __forceinline__ float epilogue_scalars(const DenseFwdParams& p, const
 // One normalisation, one rounding, stores straight from the accumulator layout.
 template <typename T, int DB>
 __device__ __forceinline__ void epilogue(const DenseFwdParams& p, const Tile& w, const Cols& c,
-                                         const Softmax& st, const f32x16 (&o)[DB], bool full_sum = false) {
-  const float inv = epilogue_scalars(p, w, c, st, full_sum);
+                                         const Softmax& st, const f32x16 (&o)[DB]) {
+  const float inv = epilogue_scalars(p, w, c, st);
   if (c.tq < w.t_end) {
     T* ob = (T*)p.out + (int64_t)c.tq * p.o_st + (int64_t)c.hq * p.o_sh;
 #pragma unroll
@@ -242,8 +230,6 @@ struct Bf {
   static constexpr int kDmaPerWave = kTileUnits / 64 / 4;
   static constexpr int kQFrags = D / 16;
   static constexpr int kDBlocks = D / 32;
-  // row sums on the MFMA unit (an extra all-ones block of V^T) where registers allow
-  static constexpr bool kMfmaRowSum = D == 128;
   static_assert(kTileUnits % 256 == 0, "tile must split evenly over the four waves");
 };
 
@@ -377,11 +363,10 @@ __device__ __forceinline__ bf16x8 v_frag(const u32x4* vbuf, const VOffsets<D>& v
   return __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// O^T += V^T P^T for the tile in `vbuf` (probabilities in sc); with the MFMA row sum,
-// lacc += 1 P^T as well.
+// O^T += V^T P^T for the tile in `vbuf` (probabilities in sc).
 template <int D>
 __device__ __forceinline__ void pv_tile(const u32x4* vbuf, const f32x16 (&sc)[2], const VOffsets<D>& vo,
-                                        f32x16 (&o)[Bf<D>::kDBlocks], f32x16& lacc) {
+                                        f32x16 (&o)[Bf<D>::kDBlocks]) {
   using B = Bf<D>;
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
@@ -391,7 +376,6 @@ __device__ __forceinline__ void pv_tile(const u32x4* vbuf, const f32x16 (&sc)[2]
     const bf16x8 pb = cvt_bf16x8(pf);
 #pragma unroll
     for (int d = 0; d < B::kDBlocks; ++d) o[d] = mfma_bf16_32x32x16(v_frag<D>(vbuf, vo, ks, d), pb, o[d]);
-    if constexpr (B::kMfmaRowSum) lacc = mfma_bf16_32x32x16(kOnesBf16x8, pb, lacc);
   }
 }
 
@@ -404,7 +388,7 @@ template <int D>
 __device__ __forceinline__ float qk_pv_step(const u32x4* kbuf, const u32x4* vbuf, const bf16x8 (&qf)[Bf<D>::kQFrags],
                                             int kaddr, const VOffsets<D>& vo, f32x16 (&sn)[2],
                                             const f32x16 (&sc)[2], float c2, float mu, f32x16 (&o)[Bf<D>::kDBlocks],
-                                            f32x16& lacc, float& sn_max) {
+                                            float& sn_max) {
   using B = Bf<D>;
   constexpr int NQ = 2 * B::kQFrags;  // QK^T MFMAs (32 for D = 256, 16 for D = 128, 8 for D = 64)
   constexpr int NP = 4 * B::kDBlocks; // PV MFMAs
@@ -443,24 +427,19 @@ __device__ __forceinline__ float qk_pv_step(const u32x4* kbuf, const u32x4* vbuf
       asm volatile("" : "+v"(pf[x & 7]));  // this slot's exponentials stay in this slot
       if ((x & 7) == 7) {
         pb[x >> 3] = cvt_bf16x8(pf);
-        if constexpr (!B::kMfmaRowSum) {
 #pragma unroll
-          for (int h = 0; h < 8; ++h) rs += pf[h];
-        }
+        for (int h = 0; h < 8; ++h) rs += pf[h];
       }
     }
     __builtin_amdgcn_sched_barrier(0);
   }
-  if constexpr (!B::kMfmaRowSum) asm volatile("" ::"v"(rs));  // the row sum is finished inside the stream
+  asm volatile("" ::"v"(rs));  // the row sum is finished inside the stream
   // the 16 max steps (two new scores each) over the NP PV slots: steps [16 i / NP, 16 (i + 1) / NP)
   float mx = -INFINITY;
 #pragma unroll
   for (int i = 0; i < NP; ++i) {
     const int ks = i / B::kDBlocks, d = i % B::kDBlocks;
     o[d] = mfma_bf16_32x32x16(__builtin_bit_cast(bf16x8, frag[NQ + i]), pb[ks], o[d]);
-    if constexpr (B::kMfmaRowSum) {
-      if (d == B::kDBlocks - 1) lacc = mfma_bf16_32x32x16(kOnesBf16x8, pb[ks], lacc);
-    }
     if (NQ + i + kAhead < NQ + NP) read(NQ + i + kAhead);
 #pragma unroll
     for (int e = 16 * i / NP; e < 16 * (i + 1) / NP; ++e) {
@@ -505,7 +484,6 @@ __global__ __launch_bounds__(kThreads, D == 64 ? SWA_OCC64 : D == 128 ? 2 : 1) v
   f32x16 o[B::kDBlocks];
 #pragma unroll
   for (int d = 0; d < B::kDBlocks; ++d) o[d] = f32x16{};
-  f32x16 lacc = f32x16{};  // MFMA row sums (every row holds the column's sum)
   Softmax st{-INFINITY, 0.f};
   const float c2 = p.c2;
   const int nt = c.n_tiles;
@@ -544,10 +522,10 @@ __global__ __launch_bounds__(kThreads, D == 64 ? SWA_OCC64 : D == 128 ? 2 : 1) v
     barrier_keep_loads();  // K(j), V(j-1) landed for every wave; K(j-1), V(j-2) consumed
     if (j + 1 < nt) dma_tile<D, false>(kbase, p.k_st, kb + kBN, c.k_hi, knext, c.wave, c.lane, kdl);
     dma_tile<D, true>(vbase, p.v_st, kb, c.k_hi, vcur_dst, c.wave, c.lane, vdl);
-    rescale_o<B::kDBlocks>(ts.move, ts.alpha, o, lacc);
+    rescale_o<B::kDBlocks>(ts.move, ts.alpha, o);
     f32x16 sn[2];
     float sn_max;
-    const float rs = qk_pv_step<D>(kcur, vprev, qf, kaddr, vo, sn, sc, c2, ts.mu, o, lacc, sn_max);
+    const float rs = qk_pv_step<D>(kcur, vprev, qf, kaddr, vo, sn, sc, c2, ts.mu, o, sn_max);
     if (tile_needs_mask(c, kb)) {  // diagonal / window-edge tile: mask, then take the max again
       mask_tile(sn, kb, c);
       sn_max = lane_max(sn);
@@ -566,15 +544,14 @@ __global__ __launch_bounds__(kThreads, D == 64 ? SWA_OCC64 : D == 128 ? 2 : 1) v
   // last tile: its V is in buffer (nt - 1) & 1
   wait_vm0();
   barrier_keep_loads();
-  rescale_o<B::kDBlocks>(ts.move, ts.alpha, o, lacc);
+  rescale_o<B::kDBlocks>(ts.move, ts.alpha, o);
   st.l = st.l * ts.alpha + tile_exp(sc, c2, ts.mu);
-  if ((nt - 1) & 1) pv_tile<D>(v1, sc, vo, o, lacc);
-  else pv_tile<D>(v0, sc, vo, o, lacc);
-  if constexpr (B::kMfmaRowSum) st.l = lacc[0];
+  if ((nt - 1) & 1) pv_tile<D>(v1, sc, vo, o);
+  else pv_tile<D>(v0, sc, vo, o);
   // every wave is past its last K read (the barrier above): the K buffers hold the output
   // images, two waves per buffer
   char* img = (char*)(c.wave < 2 ? k0 : k1) + (c.wave & 1) * (64 * D);
-  const float inv = epilogue_scalars(p, w, c, st, B::kMfmaRowSum);
+  const float inv = epilogue_scalars(p, w, c, st);
   store_out_bf16<D>(p, w, c, inv, o, img);
 }
 
