@@ -55,8 +55,6 @@ constexpr float kRescaleLog2 = 8.f;  // lazy-rescale threshold (log2 units)
 #define SWA_OCC64 3
 #endif
 
-typedef __attribute__((address_space(1))) const void glob_cvoid;
-
 template <typename T, int D>
 __device__ __forceinline__ void write_padding(const DenseFwdParams& p, const Tile& w) {
   // zero rows [t0, t_end) x heads [h0, h0 + HB); lse = -inf
