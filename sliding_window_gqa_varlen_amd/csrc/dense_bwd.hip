@@ -310,18 +310,11 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(DenseBwdParams p) {
     tile(k0, v0, c.k_lo + j * kBN);
   }
 
-  if (c.tq < w.t_end) {
-    __bf16* ob = (__bf16*)p.dq + (int64_t)c.tq * p.dq_st + (int64_t)c.hq * p.dq_sh + 4 * c.h2;
-#pragma unroll
-    for (int d = 0; d < B::DB; ++d)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        f32x4 r;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) r[e] = acc[d][4 * i + e] * f.scale;
-        *(bf16x4*)(ob + 32 * d + 8 * i) = cvt_bf16x4(r);
-      }
-  }
+  // the last tile was read from buffer pair (nt - 1) & 1; every wave finished the other pair
+  // before the last barrier and no transfer targets it: it holds the output images, two waves
+  // per buffer
+  char* img = (char*)(((nt - 1) & 1) ? (c.wave < 2 ? k0 : v0) : (c.wave < 2 ? k1 : v1)) + (c.wave & 1) * (64 * D);
+  store_out_bf16<D>(p.dq, p.dq_st, p.dq_sh, w, c, f.hb_shift, f.scale, acc, img);
 }
 
 // ======================================================================================

@@ -1,7 +1,8 @@
 // Device helpers shared by the dense forward and backward kernels (gfx950): packed-document
-// tile decoding (segment binary search over cu_seqlens, XCD-aware block placement), the
-// per-lane query-column geometry of a 128-column workgroup, and the causal / window mask of
-// one 64-key tile in the transposed-score layout (lane = query column, rows = keys).
+// tile decoding (segment search over cu_seqlens, XCD-aware block placement), the per-lane
+// query-column geometry of a 128-column workgroup, the causal / window mask of one 64-key
+// tile in the transposed-score layout (lane = query column, rows = keys), and the
+// LDS-staged bf16 store of a wave's 32 output columns.
 #pragma once
 
 #include "device_common.h"
@@ -156,6 +157,44 @@ __device__ __forceinline__ void mask_tile(f32x16 (&sc)[2], int kb, const Cols& c
       const int off = 32 * blk + 8 * (a >> 2) + (a & 3);
       sc[blk][a] = (unsigned)(off - lo) <= range ? sc[blk][a] : -INFINITY;
     }
+}
+
+// bf16 output of one wave through LDS, scaled by `mult`.  The wave's 32 query columns are
+// 32 rows of D values; lane (n, h2) holds dims 32 d + 8 i + 4 h2 + (0..3) of column n.  Each
+// lane writes its bf16 quads into a wave-private image of 64 D bytes (column n at n * 2D
+// bytes, 16-byte unit u at u ^ key(n) so a half-wave's writes spread over the banks), then
+// reads it back 16 bytes per lane: one store instruction writes 64 consecutive units = whole
+// rows of 512 / D adjacent columns, and columns with adjacent heads of one token are adjacent
+// in memory.  Direct stores from the accumulator layout would touch 32 rows with 8 bytes each
+// per instruction.
+template <int D>
+__device__ __forceinline__ int out_key(int n) {
+  if constexpr (D == 64) return (n >> 1) & 7;
+  else return n & 15;
+}
+template <int D>
+__device__ __forceinline__ void store_out_bf16(void* out, int64_t st, int64_t sh, const Tile& w, const Cols& c,
+                                               int hb_shift, float mult, const f32x16 (&o)[D / 32], char* img) {
+  constexpr int U = D / 8;           // 16-byte units per column
+  constexpr int kCols = 512 / D;     // columns per store instruction
+#pragma unroll
+  for (int d = 0; d < D / 32; ++d)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f32x4 r;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) r[e] = o[d][4 * i + e] * mult;
+      *(bf16x4*)(img + c.n * (2 * D) + (((4 * d + i) ^ out_key<D>(c.n)) << 4) + 8 * c.h2) = cvt_bf16x4(r);
+    }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's own writes, in order
+  const int u = c.lane % U;
+#pragma unroll
+  for (int k = 0; k < 32 / kCols; ++k) {
+    const int n = k * kCols + c.lane / U;
+    const u32x4 val = *(const u32x4*)(img + n * (2 * D) + ((u ^ out_key<D>(n)) << 4));
+    const int t = c.tw0 + (n >> hb_shift);
+    if (t <= c.tw1) *(u32x4*)((__bf16*)out + (int64_t)t * st + (int64_t)(w.h0 + (n & (w.HB - 1))) * sh + 8 * u) = val;
+  }
 }
 
 }  // namespace

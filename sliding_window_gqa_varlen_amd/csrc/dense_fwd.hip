@@ -180,44 +180,6 @@ __device__ __forceinline__ void epilogue(const DenseFwdParams& p, const Tile& w,
   }
 }
 
-// bf16 output of one wave through LDS.  The wave's 32 query columns are 32 rows of D
-// values; lane (n, h2) holds dims 32 d + 8 i + 4 h2 + (0..3) of column n.  Each lane writes
-// its bf16 quads into a wave-private image (column n at n * 2D bytes, 16-byte unit u at
-// u ^ key(n) so a half-wave's writes spread over the banks), then reads it back 16 bytes per
-// lane: one store instruction writes 64 consecutive units = whole rows of 512 / D adjacent
-// columns, and columns with adjacent heads of one token are adjacent in memory.  Direct
-// stores from the accumulator layout would touch 32 rows with 8 bytes each per instruction.
-template <int D>
-__device__ __forceinline__ int out_key(int n) {
-  if constexpr (D == 64) return (n >> 1) & 7;
-  else return n & 15;
-}
-template <int D>
-__device__ __forceinline__ void store_out_bf16(const DenseFwdParams& p, const Tile& w, const Cols& c, float inv,
-                                               const f32x16 (&o)[D / 32], char* img) {
-  constexpr int U = D / 8;           // 16-byte units per column
-  constexpr int kCols = 512 / D;     // columns per store instruction
-#pragma unroll
-  for (int d = 0; d < D / 32; ++d)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      f32x4 r;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) r[e] = o[d][4 * i + e] * inv;
-      *(bf16x4*)(img + c.n * (2 * D) + (((4 * d + i) ^ out_key<D>(c.n)) << 4) + 8 * c.h2) = cvt_bf16x4(r);
-    }
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's own writes, in order
-  const int u = c.lane % U;
-#pragma unroll
-  for (int k = 0; k < 32 / kCols; ++k) {
-    const int n = k * kCols + c.lane / U;
-    const u32x4 val = *(const u32x4*)(img + n * (2 * D) + ((u ^ out_key<D>(n)) << 4));
-    const int t = c.tw0 + (n >> p.hb_shift);
-    if (t <= c.tw1)
-      *(u32x4*)((__bf16*)p.out + (int64_t)t * p.o_st + (int64_t)(w.h0 + (n & (w.HB - 1))) * p.o_sh + 8 * u) = val;
-  }
-}
-
 // ======================================================================================
 // bf16: DMA-staged, software-pipelined kernel
 // ======================================================================================
@@ -550,7 +512,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? SWA_OCC64 : D == 128 ? 2 : 1) v
   // images, two waves per buffer
   char* img = (char*)(c.wave < 2 ? k0 : k1) + (c.wave & 1) * (64 * D);
   const float inv = epilogue_scalars(p, w, c, st);
-  store_out_bf16<D>(p, w, c, inv, o, img);
+  store_out_bf16<D>(p.out, p.o_st, p.o_sh, w, c, p.hb_shift, inv, o, img);
 }
 
 // ======================================================================================
