@@ -18,7 +18,8 @@
 //    P^T = exp2(S^T c2 - lse_col) and dS^T = P^T (dP^T - delta_col) are lane-local; then
 //    dQ^T += K^T dS^T with the K^T operand read transposed from LDS (ds_read_b64_tr_b16).
 //    Its prologue computes delta = <dout, out> of the lane's column (the two half-waves each
-//    hold half the coordinates) and writes it for the dk/dv and dsink kernels, which run after.
+//    hold half the coordinates) and writes it for the dk/dv and dsink kernels, which run after;
+//    its dq tile leaves through the idle LDS buffer pair so every store writes whole rows.
 //  * dk/dv kernel (key-parallel): a workgroup owns 128 keys of one KV head (32 per wave with
 //    32x32 MFMAs for head_dim 64, 16 per wave of 8 waves with 16x16x32 MFMAs for head_dim 128;
 //    their K and V rows held in registers) and walks the 64-query tiles of every query head

@@ -18,20 +18,22 @@
 //    O^T += V^T P^T.  V stays row-major in LDS; its transposed A operand comes from
 //    ds_read_b64_tr_b16.
 //  * Per-document tiling.  Query tiles start at document starts (virtual tile index
-//    v -> segment by binary search over cu_seqlens, no host round trip), key tiles cover
+//    v -> segment by one ballot over cu_seqlens held one boundary per lane, or a binary
+//    search beyond 61 documents; no host round trip), key tiles cover
 //    only [max(doc start, first query - window + 1), last query]; masks are evaluated
 //    only on tiles that straddle the diagonal or the window edge.
 //  * Scheduling.  Blocks are remapped so that all tiles of one KV head land on the same
 //    XCD (its L2 holds that head's K/V), and each document's tiles run last-first
-//    (heaviest first for causal masks).
-//  * bf16 pipeline.  64-key K and V tiles arrive by global_load_lds_dwordx4 straight into
+//    (heaviest first for causal masks).  XCDs that share a head chunk under a causal mask
+//    deal its tiles round robin.
+//  * bf16 pipeline.  64-key K and V tiles arrive by buffer_load ... lds straight into
 //    two LDS buffers each (no register staging); iteration j issues the MFMAs of
 //    S(j) = K(j) Q^T, runs the online softmax of tile j-1 in their shadow, then
 //    O += V(j-1) P(j-1), while K(j+1) and V(j) are in flight.  Buffers are separate
 //    __shared__ arrays named statically (the loop is unrolled by two), so no LDS read
 //    waits on a transfer into another buffer.  Rows are XOR-swizzled for the 64-bank
 //    LDS: K for row reads of 16 rows at one unit, V for transposed reads of 4 rows x 4
-//    units.
+//    units.  The output tile leaves through LDS so that every store writes whole rows.
 //  * Online softmax with lazy rescaling: the reference maximum moves only when a score
 //    exceeds it by more than 2^8 (probabilities stay <= 256), so most tiles skip the O
 //    rescale; the final normalisation uses the same reference, so the result is exact.

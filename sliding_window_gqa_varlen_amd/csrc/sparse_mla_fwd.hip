@@ -16,11 +16,12 @@
 //  * The index row is first compacted in LDS to the slots that are valid (in range,
 //    causal, same document), so invalid slots cost neither gather bytes nor MFMA work.
 //  * Chunks of 32 compacted slots are gathered straight into LDS with
-//    global_load_lds_dwordx4 (no register staging): 32 rows x 72 16-byte units
+//    buffer_load ... lds (no register staging): 32 rows x 72 16-byte units
 //    (64 latent + 8 rotary), unit index swizzled per row so the row reads of the QK^T
-//    operand and the ds_read_b64_tr_b16 reads of the PV operand avoid bank conflicts.  Three buffers: the gather of chunk c+2 is issued right after the score
-//    exchange of chunk c, and the loop is unrolled by three so every LDS read names its
-//    buffer statically (no conservative wait on the gathers in flight).
+//    operand and the ds_read_b64_tr_b16 reads of the PV operand avoid bank conflicts.
+//    Three buffers: the gather of chunk c+2 is issued right after the score exchange of
+//    chunk c, and the loop is unrolled by three so every LDS read names its buffer
+//    statically (no conservative wait on the gathers in flight).
 //  * S^T = KV Q^T (slots = M, heads = N); online softmax with lazy rescaling (the
 //    reference maximum moves only when a score exceeds it by more than 2^8, which keeps
 //    probabilities <= 256 and the result exact); O^T += latent^T P^T.
