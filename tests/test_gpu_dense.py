@@ -192,6 +192,25 @@ def test_many_documents_both_segment_decodes(gpu, n_docs, D, window):
     assert np.all(out[:7] == 0) and np.all(np.isneginf(lse[:7]))
 
 
+@pytest.mark.parametrize("D,window,sinks", [(128, 0, False), (64, 0, True), (128, 300, True)])
+def test_scores_growing_along_the_keys(gpu, D, window, sinks):
+    """Every query's scores grow by 0.08 to 0.11 per key (5 to 7 per 64-key tile), so the
+    running maximum keeps moving: the lazy reference is exceeded by more than 2^8 every few
+    tiles and the O rescale runs inside the loop, not only on the first tile."""
+    inp = custom([700, 333], T=1033, Hq=8, Hkv=2, D=D, window=window, dtype="bf16", sinks=sinks, seed=D + window)
+    T = 1033
+    pos = np.concatenate([np.arange(700), np.arange(333)]).astype(np.float32)
+    u = np.ones(D, np.float32)
+    # q . k = D * 0.01 * pos (+ noise); times scale = D^-1/2 the score grows by 0.01 sqrt(D) per key
+    q = np.broadcast_to(u, (T, 8, D)) + 0.05 * inp["q"]
+    k = (0.01 * pos)[:, None, None] * np.broadcast_to(u, (T, 2, D)) + 0.05 * inp["k"]
+    inp["q"] = W.round_to_bf16(np.ascontiguousarray(q, np.float32))
+    inp["k"] = W.round_to_bf16(np.ascontiguousarray(k, np.float32))
+    ref_o, ref_l = oracle_full(inp)
+    out, lse = run_dense(inp, "bf16")
+    assert_dense_parity("bf16", out, lse, ref_o, ref_l)
+
+
 def test_single_token_documents(gpu):
     inp = custom([1] * 300, T=300, Hq=8, Hkv=8, D=128, window=0, dtype="f32", seed=6)
     out, lse = run_dense(inp, "f32")

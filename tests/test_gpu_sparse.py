@@ -166,6 +166,23 @@ def test_long_index_rows_span_segments(gpu):
     assert metrics.sparse_valid_slots(inp["indices"], inp["doc_ids"]) > 0
 
 
+def test_scores_growing_along_the_slots(gpu):
+    """Rotary key rows whose dot product with every query grows with the key position (the
+    rotary part enters the scores but not the values, so outputs stay O(1)), and index rows in
+    ascending order: the running maximum keeps moving chunk after chunk, so the lazy O rescale
+    runs inside the chunk loop."""
+    inp = small(T=1500, topk=512, lengths=[1500], seed=9)
+    T = 1500
+    pos = np.arange(T, dtype=np.float32)
+    inp["k_pe"] = W.round_to_bf16((0.01 * pos)[:, None] + 0.05 * inp["k_pe"])
+    q = inp["q"].copy()
+    q[:, :, 512:] = 1.0
+    inp["q"] = W.round_to_bf16(q)
+    ref_o, ref_l = oracle(inp)
+    out, lse = run_sparse(inp)
+    check(out, lse, ref_o, ref_l)
+
+
 def test_repeat_runs_are_bitwise_identical(gpu):
     inp = small(400, 128, seed=15)
     o0, l0 = run_sparse(inp)
