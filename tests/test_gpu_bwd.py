@@ -204,6 +204,22 @@ def test_many_documents(gpu, n_docs, window):
         assert np.all(g[T0:] == 0)
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_scores_growing_along_the_keys(gpu, D):
+    """Scores that grow by 0.08 to 0.11 per key span more than 60 natural units along a
+    document: P = exp(S scale - lse) then ranges over many orders of magnitude per row."""
+    lengths = [700, 333]
+    inp = custom(lengths, T=1033, Hq=8, Hkv=2, window=0, sinks=True, seed=D + 3, D=D)
+    T = 1033
+    pos = np.concatenate([np.arange(700), np.arange(333)]).astype(np.float32)
+    u = np.ones(D, np.float32)
+    inp["q"] = W.round_to_bf16(np.ascontiguousarray(np.broadcast_to(u, (T, 8, D)) + 0.05 * inp["q"], np.float32))
+    inp["k"] = W.round_to_bf16(np.ascontiguousarray(
+        (0.01 * pos)[:, None, None] * np.broadcast_to(u, (T, 2, D)) + 0.05 * inp["k"], np.float32))
+    do = dout_for(inp, D)
+    check_all(run_bwd(inp, do), oracle_bwd(inp, do), inp, do)
+
+
 def test_packed_documents_elementwise(gpu):
     """2048 tokens in documents of 128..512 tokens, 16 query / 4 KV heads, full causal."""
     w = W.DenseWorkload("bwd", "bf16", T=2048, Hq=16, Hkv=4, D=128, window=0, scale=1.0 / math.sqrt(128.0),
