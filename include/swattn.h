@@ -39,7 +39,10 @@
  *    memory, keeps no per-call state and performs no host<->device copy or
  *    synchronisation: a call validates its arguments on the host, enqueues its
  *    kernels on `stream` (a hipStream_t; NULL = the legacy default stream) and
- *    returns. Buffers must stay valid until that stream work completes.
+ *    returns. Buffers must stay valid until that stream work completes. A call
+ *    enqueues kernel launches only (no memset, copy or event), so it may be captured
+ *    into a HIP graph; a replay reads the buffers captured, with their contents at
+ *    replay time.
  *  - Outputs must not alias inputs.
  *  - Return value: SWA_OK (0) or a negative swa_status. On any error detected on the
  *    host nothing is enqueued and the outputs are untouched; swa_last_error() then
