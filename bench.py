@@ -365,9 +365,17 @@ def main() -> int:
     elif getattr(wl, "backward", False):
         achieved = flops / (ms * 1e-3) / 1e12
         value = achieved
-        roof = metrics.roofline("mfma", achieved, metrics.MI355X_BF16_DENSE_TFLOPS, "TFLOP/s", traffic)
+        min_bytes = metrics.dense_bwd_min_bytes(wl.T, wl.Hq, wl.Hkv, wl.D, inp["n_docs"], wl.sinks)
+        hbm_gbps = min_bytes / (ms * 1e-3) / 1e9
+        # the roofline that binds, as for the forward
+        if flops / min_bytes < metrics.MI355X_BF16_DENSE_TFLOPS * 1e12 / (metrics.MI355X_HBM_GBPS * 1e9):
+            roof = metrics.roofline("hbm", hbm_gbps, metrics.MI355X_HBM_GBPS, "GB/s", traffic)
+        else:
+            roof = metrics.roofline("mfma", achieved, metrics.MI355X_BF16_DENSE_TFLOPS, "TFLOP/s", traffic)
         metric, unit = "packed GQA attn bwd mask-effective TFLOP/s + % bf16 MFMA peak (1 GPU)", "TFLOP/s"
         config["pct_bf16_mfma_peak"] = 100.0 * achieved / metrics.MI355X_BF16_DENSE_TFLOPS
+        config["min_hbm_gbps"] = hbm_gbps
+        config["arithmetic_intensity"] = flops / min_bytes
     elif sparse:
         achieved = work / (ms * 1e-3) / 1e9
         value = achieved

@@ -59,6 +59,17 @@ def dense_min_bytes(T: int, Hq: int, Hkv: int, D: int, elem_bytes: int, n_docs: 
     return b
 
 
+def dense_bwd_min_bytes(T: int, Hq: int, Hkv: int, D: int, n_docs: int, with_sinks: bool = False) -> int:
+    """Backward HBM minimum (bf16): q, out, dout [T, Hq, D], k, v [T, Hkv, D] and the fp32 lse
+    [T, Hq] read once; dq, dk, dv written once; cu_seqlens read, sinks read and dsinks written."""
+    b = 2 * D * T * (3 * Hq + 2 * Hkv) + 4 * T * Hq
+    b += 2 * D * T * (Hq + 2 * Hkv)
+    b += 4 * (n_docs + 1)
+    if with_sinks:
+        b += 2 * 4 * Hq
+    return b
+
+
 def sparse_valid_slots(indices: np.ndarray, doc_ids: np.ndarray) -> int:
     """Slots that name an in-range, causal, same-document key (duplicates count per slot)."""
     T = indices.shape[0]

@@ -86,3 +86,13 @@ def test_sparse_indices_are_causal_same_document_sorted_distinct():
             assert sel[0] >= start and sel[-1] <= t
         start += L
     assert metrics.sparse_valid_slots(idx, ids) == metrics.sparse_generated_slots(lengths, w.topk)
+
+
+def test_backward_minimum_bytes_count_every_tensor_once():
+    """q, out, dout, dq [T, Hq, D] and k, v, dk, dv [T, Hkv, D] in bf16, lse fp32, cu_seqlens,
+    sinks and dsinks: counted tensor by tensor for a small shape."""
+    T, Hq, Hkv, D, n_docs = 10, 4, 2, 8, 3
+    per_q, per_kv = T * Hq * D * 2, T * Hkv * D * 2
+    want = 4 * per_q + 4 * per_kv + 4 * T * Hq + 4 * (n_docs + 1)
+    assert metrics.dense_bwd_min_bytes(T, Hq, Hkv, D, n_docs) == want
+    assert metrics.dense_bwd_min_bytes(T, Hq, Hkv, D, n_docs, with_sinks=True) == want + 2 * 4 * Hq
