@@ -46,6 +46,9 @@ constexpr int kTK = 128;           // keys per dk/dv workgroup
 #ifndef SWA_BWD_AHEAD
 #define SWA_BWD_AHEAD 8
 #endif
+#ifndef SWA_DQ_OCC64
+#define SWA_DQ_OCC64 3  // head_dim 64 dq: 3 waves / SIMD (168 VGPRs, 2 dwords spilled outside the loop)
+#endif
 #ifndef SWA_BWD_AHEAD64
 #define SWA_BWD_AHEAD64 4
 #endif
@@ -202,7 +205,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dsink_reduce_kernel(DenseBwdPara
 // dq: query-parallel, the forward's tiles
 // ======================================================================================
 template <int D>
-__global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(DenseBwdParams p) {
+__global__ __launch_bounds__(kThreads, D == 64 ? SWA_DQ_OCC64 : 2) void bwd_dq_kernel(DenseBwdParams p) {
   using B = Bw<D>;
   __shared__ u32x4 k0[B::TileUnits];
   __shared__ u32x4 k1[B::TileUnits];
