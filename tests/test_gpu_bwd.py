@@ -252,6 +252,19 @@ def test_full_size_workloads_on_chosen_documents(gpu, idx):
             check(g[sl], r, f"{name} of document {d} ({e - s} tokens)", x)
 
 
+def test_causal_workload_every_element(gpu):
+    """The 8192-token causal backward as bench times it (out and lse from the GPU forward): every
+    element of dq, dk and dv against the fp64 oracle over all documents (about 30 s of host time)."""
+    inp = W.make_dense(W.WORKLOADS[1])
+    do = dout_for(inp, 11)
+    out, lse = gpu_forward(inp)
+    got = run_bwd(inp, do, out=out, lse=lse)
+    args = (inp["q"], inp["k"], inp["v"], do, inp["cu_seqlens"], inp["window"], inp["scale"], inp["sinks"])
+    ref = varlen_attn_bwd_ref(*args)
+    for name, g, r, x in zip(("dq", "dk", "dv"), got[:3], ref[:3], term_rss(*args)):
+        check(g, r, name, x)
+
+
 def test_with_the_gpu_forward_outputs(gpu):
     """out and lse straight from varlen_attn_fwd (bf16 out, fp32 lse) feed the backward."""
     lengths = [120, 300, 80]
