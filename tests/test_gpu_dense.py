@@ -95,10 +95,11 @@ def test_bf16_workloads_full_size_sampled(gpu, idx):
     assert err_l <= BF16_MAX_ABS, err_l
 
 
-def test_headline_workload_every_row(gpu):
-    """The 8192-token causal workload exactly as bench times it, every (token, head) row of out
-    and lse against the full fp64 oracle (about 10 s of host time)."""
-    inp = W.make_dense(W.WORKLOADS[1])
+@pytest.mark.parametrize("idx", [1, 2, 3])
+def test_bf16_workloads_full_size_every_row(gpu, idx):
+    """The full-size workloads exactly as bench times them, every (token, head) row of out and
+    lse against the full fp64 oracle (about 5, 15 and 30 s of host time)."""
+    inp = W.make_dense(W.WORKLOADS[idx])
     out, lse = run_dense(inp, "bf16")
     ref_o, ref_l = oracle_full(inp)
     assert_dense_parity("bf16", out, lse, ref_o, ref_l)
