@@ -311,3 +311,11 @@ def test_head_dim_256_packed_documents_elementwise(gpu):
     ref_o, ref_l = oracle_full(inp)
     out, lse = run_dense(inp, "bf16")
     assert_dense_parity("bf16", out, lse, ref_o, ref_l)
+
+
+def test_head_dim_256_workload_full_size_every_row(gpu):
+    """The 8192-token head_dim-256 causal workload exactly as bench times it, every row."""
+    inp = W.make_dense([w for w in W.EXTRA_WORKLOADS if w.name == "causal_gqa_d256_bf16_t8192"][0])
+    out, lse = run_dense(inp, "bf16")
+    ref_o, ref_l = oracle_full(inp)
+    assert_dense_parity("bf16", out, lse, ref_o, ref_l)
