@@ -17,8 +17,11 @@
  *                   (nemo_automodel.components.models.mistral_large4.attention page).
  *
  *  varlen_attn_bwd  Its backward: dq, dk, dv (and dsink) of a loss through out, from
- *                   the forward's output and log-sum-exp (the pages keep the LSE for
- *                   the backward and call the attention differentiable).
+ *                   the forward's output and log-sum-exp. The pages return only the
+ *                   attention output and print no backward; they call sparse_mla's
+ *                   value weight differentiable (mistral_large4.attention page). The
+ *                   LSE export of varlen_attn_fwd and its use here to recompute the
+ *                   probabilities are this library's own design choice.
  *
  *  sparse_mla_fwd   Sparse MLA forward: each query token attends to the top-k key
  *                   rows its index row names; a key is a shared 512-wide latent row

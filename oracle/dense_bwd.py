@@ -2,11 +2,11 @@
 
 TEST INFRASTRUCTURE ONLY (see the package docstring).
 
-The pages state that the attention is differentiable and that its log-sum-exp
-is kept for the backward pass (``MuseMagiPlan.attention`` on the muse_spark
-magi_cp page returns the output with its LSE; ``sparse_mla`` on the
-mistral_large4 attention page is differentiable); they print no backward
-formulas.  The gradient of a loss L that depends on ``out`` is the unique
+The pages print no backward formulas.  ``MuseMagiPlan.attention`` on the
+muse_spark magi_cp page returns only the attention output (no log-sum-exp);
+``sparse_mla`` on the mistral_large4 attention page calls its value weight
+differentiable, and ``MistralLarge4Attention.forward`` keeps a shared KV that is
+never detached, so gradients flow through attention.  The gradient of a loss L that depends on ``out`` is the unique
 derivative of the forward definition (``dense.varlen_attn_ref``), so this
 module writes it out by the chain rule.  For every document [s, e), query token
 i in it, query head h with KV head g = h // G, and allowed keys j

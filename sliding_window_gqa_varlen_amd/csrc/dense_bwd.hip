@@ -3,8 +3,9 @@
 //
 // Operation: the gradients of a loss through `out` of the forward in dense_fwd.hip
 // (MuseMagiPlan.attention on the muse_spark magi_cp page, FlintMagiPlan.attention on the
-// flint magi page, GQA of MuseGlimmerAttention on the muse_glimmer model page), with the
-// forward's log-sum-exp `lse` (sink included) kept from the forward pass:
+// flint magi page, GQA of MuseGlimmerAttention on the muse_glimmer model page).  The pages
+// print no backward and return no log-sum-exp; recomputing the probabilities from the
+// forward's exported `lse` (sink included) is this library's own design:
 //   P_ij = exp(scale q_i.k_j - lse_i)     delta_i = <dout_i, out_i>
 //   dS_ij = P_ij (<dout_i, v_j> - delta_i)
 //   dq_i = scale sum_j dS_ij k_j ;  dk_j = scale sum_{i,h} dS_ij q_i ;  dv_j = sum_{i,h} P_ij dout_i

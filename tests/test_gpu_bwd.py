@@ -1,23 +1,34 @@
 """GPU parity of varlen_attn_bwd (through the C ABI) against the fp64 backward oracle.
 
-The HIP path receives the oracle forward's output (rounded to bf16) and log-sum-exp (rounded
-to fp32) and the same seeded dout; its dq, dk, dv, dsinks are compared element by element.
+The HIP path receives a forward output `out` (the oracle's, rounded to bf16, or the GPU
+forward's), the matching log-sum-exp and the same seeded dout; its dq, dk, dv, dsinks are
+compared element by element with the exact (fp64) gradients.
 
-Tolerance: |got - ref| <= 2e-2 * max(1, |ref|) + 6 * 2^-9 * rss, where rss is the root sum
-of squares of the terms the element sums (dv[j]: P_ij dout[i]; dk[j]: scale dS_ij q[i];
-dq[i]: scale dS_ij k[j]).  Each gradient element is a sum of many terms of either sign (dk
-and dv over every query that sees the key, times the group's heads); the kernel rounds P and
-dS to bf16 as matrix operands (relative error at most 2^-9, independent per term), so its
-error has a standard deviation below 2^-9 rss, which can exceed 2e-2 where the terms cancel
-to a small result.  The first part is the forward's bf16 bar (one rounding of the result).
+Tolerance, per element, from the arithmetic of the kernel:
+  |got - ref| <= (2^-8 + 1e-4) |ref| + 6 * 2^-9 * rss + |e_delta| + 1e-6
+* 2^-8 |ref|: the one bf16 rounding of the result (round to nearest even, 8 significant
+  bits: relative error at most 2^-8).  1e-4 |ref| covers fp32 effects (exp2, accumulation
+  order, the fp32 lse).
+* 6 * 2^-9 * rss: rss is the root sum of squares of the terms the element sums (dv[j]:
+  P_ij dout[i]; dk[j]: scale dS_ij q[i]; dq[i]: scale dS_ij k[j]).  The kernel rounds P and
+  dS to bf16 as matrix operands; a rounding to 8 significant bits has a relative standard
+  deviation of about 2^-9, independently per term, so the sum's error has a standard deviation
+  of about 2^-9 rss; six of them bound it.  This matters where the terms cancel to a small
+  result.
+* e_delta: the kernel computes delta_i = <dout_i, out_i> from the `out` it is given, which
+  differs from the exact output (bf16 rounding, or the GPU forward's own error).  The
+  gradient error this induces is linear and computed exactly by the test:
+  dq_i: -scale (delta_used - delta)_i sum_j P_ij k_j ; dk_j: -scale sum_i P_ij (delta_used -
+  delta)_i q_i ; dv is unaffected.
 
 dsinks_h = -sum_i p_sink_i delta_i is a sum whose terms cancel (delta_i = <dout_i, out_i> has
 either sign), so a relative bar does not apply.  Its error is set by the bf16 out the kernel
 receives: rounding element e of out moves the sum by p_sink_i dout_ie out_ie times a relative
-error of at most 2^-9, independently per element, so the error has a standard deviation below
-sigma_h = 2^-9 sqrt(sum_{i,e} (p_sink_i dout_ie out_ie)^2).  The bar is 6 sigma_h +
-1e-3 * max(1, |ref|).  A second check recomputes the sum in fp64 from the very bf16 out the
-kernel was given and holds the kernel to 1e-4 of sum_i p_sink_i |delta_i| (fp32 summation).
+error of standard deviation about 2^-9, independently per element, so the error has a standard
+deviation below sigma_h = 2^-9 sqrt(sum_{i,e} (p_sink_i dout_ie out_ie)^2).  The bar is
+6 sigma_h + 1e-3 * max(1, |ref|).  A second check recomputes the sum in fp64 from the very
+bf16 out the kernel was given and holds the kernel to 1e-4 of sum_i p_sink_i |delta_i| (fp32
+summation).
 """
 import math
 
@@ -31,7 +42,7 @@ from tests.gpu_util import dev
 
 pytestmark = pytest.mark.gpu
 
-TOL = 2e-2
+ROUND = 2.0 ** -8 + 1e-4  # one bf16 rounding of the result, plus fp32 effects
 
 
 def custom(lengths, T, Hq, Hkv, window, sinks=False, seed=0, D=128):
@@ -66,7 +77,7 @@ def run_bwd(inp, do, window=None, out=None, lse=None):
                                      inp["scale"], s)
     torch.cuda.synchronize()
     f = lambda x: None if x is None else x.float().cpu().numpy().astype(np.float64)  # noqa: E731
-    return f(dq), f(dk), f(dv), f(ds)
+    return f(dq), f(dk), f(dv), f(ds), f(out)
 
 
 def oracle_bwd(inp, do, window=None):
@@ -75,43 +86,53 @@ def oracle_bwd(inp, do, window=None):
                                inp["sinks"])[:4]
 
 
-def term_rss(q, k, v, do, cu, window, scale, sinks):
-    """Root sum of squares of the terms each dq, dk, dv element sums (tolerance only)."""
+def term_rss(q, k, v, do, cu, window, scale, sinks, out_used=None):
+    """Root sum of squares of the terms each dq, dk, dv element sums, and the exact gradient
+    error that delta computed from `out_used` instead of the exact output induces in dq and dk
+    (tolerance only)."""
     q, k, v, do = (np.asarray(x, np.float64) for x in (q, k, v, do))
     T, Hq, D = q.shape
     Hkv = k.shape[1]
     G = Hq // Hkv
     rq, rk, rv = np.zeros(q.shape), np.zeros(k.shape), np.zeros(v.shape)
+    eq, ek = np.zeros(q.shape), np.zeros(k.shape)
     for d in range(len(cu) - 1):
         s, e = int(cu[d]), int(cu[d + 1])
-        if e <= s:
-            continue
-        i, j = np.arange(s, e)[:, None], np.arange(s, e)[None, :]
-        ok = (j <= i) & ((window == 0) | (i - j < window))
-        for h in range(Hq):
-            g = h // G
-            S = np.where(ok, scale * q[s:e, h] @ k[s:e, g].T, -np.inf)
-            m = S.max(axis=1)
-            if sinks is not None:
-                m = np.maximum(m, sinks[h])
-            E = np.exp(S - m[:, None])
-            Z = E.sum(axis=1) + (0.0 if sinks is None else np.exp(sinks[h] - m))
-            P = E / Z[:, None]
-            dP = do[s:e, h] @ v[s:e, g].T
-            dS = P * (dP - (P * dP).sum(axis=1, keepdims=True))
-            rv[s:e, g] += (P ** 2).T @ do[s:e, h] ** 2
-            rk[s:e, g] += scale ** 2 * (dS ** 2).T @ q[s:e, h] ** 2
-            rq[s:e, h] = scale ** 2 * (dS ** 2) @ k[s:e, g] ** 2
-    return np.sqrt(rq), np.sqrt(rk), np.sqrt(rv)
+        for i0 in range(s, e, 256):  # query blocks; keys limited to the block's causal / window range
+            i1 = min(i0 + 256, e)
+            lo = max(s, i0 - window + 1) if window > 0 else s
+            i, j = np.arange(i0, i1)[:, None], np.arange(lo, i1)[None, :]
+            ok = (j <= i) & ((window == 0) | (i - j < window))
+            for h in range(Hq):
+                g = h // G
+                S = np.where(ok, scale * q[i0:i1, h] @ k[lo:i1, g].T, -np.inf)
+                m = S.max(axis=1)
+                if sinks is not None:
+                    m = np.maximum(m, sinks[h])
+                E = np.exp(S - m[:, None])
+                Z = E.sum(axis=1) + (0.0 if sinks is None else np.exp(sinks[h] - m))
+                P = E / Z[:, None]
+                dP = do[i0:i1, h] @ v[lo:i1, g].T
+                dS = P * (dP - (P * dP).sum(axis=1, keepdims=True))
+                rv[lo:i1, g] += (P ** 2).T @ do[i0:i1, h] ** 2
+                rk[lo:i1, g] += scale ** 2 * (dS ** 2).T @ q[i0:i1, h] ** 2
+                rq[i0:i1, h] = scale ** 2 * (dS ** 2) @ k[lo:i1, g] ** 2
+                if out_used is not None:
+                    o_exact = P @ v[lo:i1, g]
+                    ddelta = (do[i0:i1, h] * (np.asarray(out_used[i0:i1, h], np.float64) - o_exact)).sum(axis=1)
+                    eq[i0:i1, h] = -scale * ddelta[:, None] * (P @ k[lo:i1, g])
+                    ek[lo:i1, g] += -scale * (P.T @ (ddelta[:, None] * q[i0:i1, h]))
+    return (np.sqrt(rq), np.sqrt(rk), np.sqrt(rv)), (np.abs(eq), np.abs(ek), np.zeros(v.shape))
 
 
-def check(got, ref, what, rss):
+def check(got, ref, what, rss, e_delta=0.0):
     assert got.shape == ref.shape, what
     assert np.all(np.isfinite(got)), f"{what}: non-finite values"
-    bar = TOL * np.maximum(1.0, np.abs(ref)) + 6 * 2.0 ** -9 * rss
+    bar = ROUND * np.abs(ref) + 6 * 2.0 ** -9 * rss + e_delta + 1e-6
     err = np.abs(got - ref) / bar
     i = np.unravel_index(np.argmax(err), err.shape)
     assert err.max() <= 1.0, f"{what}: error {err.max():.2f} x its bar at {i} (got {got[i]:.5f}, ref {ref[i]:.5f})"
+    return float(err.max())
 
 
 def sink_probabilities(inp, window=None):
@@ -123,14 +144,19 @@ def sink_probabilities(inp, window=None):
 
 
 def check_all(got, ref, inp=None, do=None, window=None, out_given=None, lse_given=None):
+    """got = (dq, dk, dv, dsinks, out the kernel received)."""
     win = inp["window"] if window is None else window
-    rss = term_rss(inp["q"], inp["k"], inp["v"], do, inp["cu_seqlens"], win, inp["scale"], inp["sinks"])
-    for name, g, r, x in zip(("dq", "dk", "dv"), got, ref, rss):
-        check(g, r, name, x)
+    rss, ed = term_rss(inp["q"], inp["k"], inp["v"], do, inp["cu_seqlens"], win, inp["scale"], inp["sinks"],
+                       out_used=got[4])
+    for name, g, r, x, e in zip(("dq", "dk", "dv"), got, ref, rss, ed):
+        check(g, r, name, x, e)
     if ref[3] is None:
         assert got[3] is None
         return
-    g, r = got[3], ref[3]
+    check_dsinks(got[3], ref[3], inp, do, window, out_given, lse_given)
+
+
+def check_dsinks(g, r, inp, do, window=None, out_given=None, lse_given=None):
     o, p = sink_probabilities(inp, window)
     d = np.asarray(do, np.float64)
     sigma = 2.0 ** -9 * np.sqrt(((p[:, :, None] * d * o) ** 2).sum(axis=(0, 2)))
@@ -247,9 +273,41 @@ def test_full_size_workloads_on_chosen_documents(gpu, idx):
         args = (inp["q"][sl], inp["k"][sl], inp["v"][sl], do[sl], [0, e - s], inp["window"], inp["scale"],
                 inp["sinks"])
         ref = varlen_attn_bwd_ref(*args)
-        rss = term_rss(*args)
-        for name, g, r, x in zip(("dq", "dk", "dv"), got[:3], ref[:3], rss):
-            check(g[sl], r, f"{name} of document {d} ({e - s} tokens)", x)
+        rss, ed = term_rss(*args, out_used=got[4][sl])
+        for name, g, r, x, err in zip(("dq", "dk", "dv"), got[:3], ref[:3], rss, ed):
+            check(g[sl], r, f"{name} of document {d} ({e - s} tokens)", x, err)
+
+
+@pytest.mark.parametrize("idx,groups", [(2, (1,)), (3, (0, 7))])
+def test_full_size_windowed_every_element_of_chosen_kv_groups(gpu, idx, groups):
+    """The full-size windowed backwards as bench times them (out and lse from the GPU forward),
+    every token: each element of dq for the query heads of the chosen KV groups, of dk and dv
+    for those KV heads, and of dsinks for those heads (the window-128 workload has sinks).
+    Groups are independent (query head h reads KV head h // G only), so the oracle runs on
+    the chosen groups alone."""
+    wl = W.WORKLOADS[idx]
+    inp = W.make_dense(wl)
+    do = dout_for(inp, 20 + idx)
+    out, lse = gpu_forward(inp)
+    got = run_bwd(inp, do, out=out, lse=lse)
+    G = wl.Hq // wl.Hkv
+    heads = [h for g in groups for h in range(g * G, (g + 1) * G)]
+    sel = dict(inp)
+    sel["q"] = inp["q"][:, heads]
+    sel["k"] = inp["k"][:, list(groups)]
+    sel["v"] = inp["v"][:, list(groups)]
+    sel["sinks"] = None if inp["sinks"] is None else np.asarray(inp["sinks"])[heads]
+    do_sel = do[:, heads]
+    ref = oracle_bwd(sel, do_sel)
+    out_sel = got[4][:, heads]
+    rss, ed = term_rss(sel["q"], sel["k"], sel["v"], do_sel, inp["cu_seqlens"], wl.window, wl.scale, sel["sinks"],
+                       out_used=out_sel)
+    sub = (got[0][:, heads], got[1][:, list(groups)], got[2][:, list(groups)])
+    for name, g, r, x, e in zip(("dq", "dk", "dv"), sub, ref[:3], rss, ed):
+        check(g, r, f"{name} of KV groups {groups}", x, e)
+    if wl.sinks:
+        check_dsinks(got[3][heads], ref[3], sel, do_sel, out_given=out_sel,
+                     lse_given=lse.cpu().numpy().astype(np.float64)[:, heads])
 
 
 def test_causal_workload_every_element(gpu):
@@ -261,8 +319,9 @@ def test_causal_workload_every_element(gpu):
     got = run_bwd(inp, do, out=out, lse=lse)
     args = (inp["q"], inp["k"], inp["v"], do, inp["cu_seqlens"], inp["window"], inp["scale"], inp["sinks"])
     ref = varlen_attn_bwd_ref(*args)
-    for name, g, r, x in zip(("dq", "dk", "dv"), got[:3], ref[:3], term_rss(*args)):
-        check(g, r, name, x)
+    rss, ed = term_rss(*args, out_used=got[4])
+    for name, g, r, x, e in zip(("dq", "dk", "dv"), got[:3], ref[:3], rss, ed):
+        check(g, r, name, x, e)
 
 
 def test_with_the_gpu_forward_outputs(gpu):
@@ -302,9 +361,10 @@ def test_strided_views_of_fused_buffers(gpu):
                     None, dq=dq, dk=dk, dv=dv)
     torch.cuda.synchronize()
     ref = oracle_bwd(inp, do)
-    rss = term_rss(inp["q"], inp["k"], inp["v"], do, inp["cu_seqlens"], 0, inp["scale"], None)
-    for name, g, r, x in zip(("dq", "dk", "dv"), (dq, dk, dv), ref[:3], rss):
-        check(g.float().cpu().numpy().astype(np.float64), r, name, x)
+    rss, ed = term_rss(inp["q"], inp["k"], inp["v"], do, inp["cu_seqlens"], 0, inp["scale"], None,
+                       out_used=W.round_to_bf16(ref_o.astype(np.float32)))
+    for name, g, r, x, e in zip(("dq", "dk", "dv"), (dq, dk, dv), ref[:3], rss, ed):
+        check(g.float().cpu().numpy().astype(np.float64), r, name, x, e)
 
 
 def test_repeat_runs_are_bitwise_identical(gpu):
