@@ -25,7 +25,7 @@ _DTYPES = {torch.float32: SWA_DTYPE_F32, torch.bfloat16: SWA_DTYPE_BF16, torch.i
 
 # functions the header declares, with their ctypes signatures
 EXPORTS = ("varlen_attn_fwd", "varlen_attn_bwd", "sparse_mla_fwd", "mla_value_proj", "swa_strerror", "swa_last_error",
-           "swa_abi_version")
+           "swa_abi_version", "swa_peak_mfma_bf16", "swa_peak_mfma_bf16_flops", "swa_peak_copy", "swa_peak_read")
 
 
 class SwaTensor(ctypes.Structure):
@@ -69,6 +69,15 @@ def load_library():
         lib.swa_last_error.restype = ctypes.c_char_p
         lib.swa_abi_version.argtypes = []
         lib.swa_abi_version.restype = i32
+        i64 = ctypes.c_int64
+        lib.swa_peak_mfma_bf16.argtypes = [vp, i32, vp]
+        lib.swa_peak_mfma_bf16.restype = i32
+        lib.swa_peak_mfma_bf16_flops.argtypes = [i32]
+        lib.swa_peak_mfma_bf16_flops.restype = ctypes.c_double
+        lib.swa_peak_copy.argtypes = [vp, vp, i64, vp]
+        lib.swa_peak_copy.restype = i32
+        lib.swa_peak_read.argtypes = [vp, i64, vp, vp]
+        lib.swa_peak_read.restype = i32
         _lib = lib
         return lib
 
@@ -89,6 +98,35 @@ def describe(t: Optional[torch.Tensor]) -> Optional[SwaTensor]:
         d.shape[i] = t.shape[i]
         d.stride[i] = t.stride(i)
     return d
+
+
+def _on_gpu(name: str, t: torch.Tensor, device: torch.device, dtype=None, contiguous: bool = False,
+            shape=None, min_numel: Optional[int] = None) -> None:
+    """Raise unless t is a tensor on `device` (a GPU) with the stated dtype / layout / size.
+
+    A host tensor would hand the kernel a host address, and a short or strided buffer behind
+    a raw pointer would be read out of bounds: both are refused before the library is called.
+    """
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU (got {t.device})")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the operands on {device}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+    if min_numel is not None and t.numel() < min_numel:
+        raise ValueError(f"{name} must hold at least {min_numel} elements (got {t.numel()})")
+
+
+def _operand_device(t: torch.Tensor) -> torch.device:
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError(f"operands must be GPU tensors (got {getattr(t, 'device', type(t))})")
+    return t.device
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -130,12 +168,19 @@ def varlen_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlen
         out = torch.empty((T, Hq, D), dtype=q.dtype, device=q.device)
     if lse is None and return_lse:
         lse = torch.empty((T, Hq), dtype=torch.float32, device=q.device)
-    if cu_seqlens is not None and cu_seqlens.dtype != torch.int32:
-        raise TypeError("cu_seqlens must be int32")
-    if sinks is not None and sinks.dtype != torch.float32:
-        raise TypeError("sinks must be float32")
-    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != (T, Hq)):
-        raise ValueError("lse must be a contiguous float32 [T, Hq] tensor")
+    dev = _operand_device(q)
+    for name, x in (("k", k), ("v", v), ("out", out)):
+        _on_gpu(name, x, dev)
+    if int(n_docs) > 0:
+        if cu_seqlens is None:
+            raise ValueError("cu_seqlens is required when n_docs > 0")
+        _on_gpu("cu_seqlens", cu_seqlens, dev, torch.int32, contiguous=True, min_numel=int(n_docs) + 1)
+    elif cu_seqlens is not None:
+        _on_gpu("cu_seqlens", cu_seqlens, dev, torch.int32, contiguous=True)
+    if sinks is not None:
+        _on_gpu("sinks", sinks, dev, torch.float32, contiguous=True, shape=(Hq,))
+    if lse is not None:
+        _on_gpu("lse", lse, dev, torch.float32, contiguous=True, shape=(T, Hq))
     dq, dk, dv, do = describe(q), describe(k), describe(v), describe(out)
     st = lib.varlen_attn_fwd(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), _ptr(cu_seqlens),
                              int(n_docs), int(window), float(scale), _ptr(sinks), ctypes.byref(do),
@@ -169,13 +214,20 @@ def varlen_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torc
         dsinks = torch.empty(Hq, dtype=torch.float32, device=q.device)
     if delta is None:
         delta = torch.empty((T, Hq), dtype=torch.float32, device=q.device)
+    dev = _operand_device(q)
+    for name, x in (("k", k), ("v", v), ("out", out), ("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv)):
+        _on_gpu(name, x, dev)
     for name, x in (("lse", lse), ("delta", delta)):
-        if x.dtype != torch.float32 or not x.is_contiguous() or tuple(x.shape) != (T, Hq):
-            raise ValueError(f"{name} must be a contiguous float32 [T, Hq] tensor")
-    if cu_seqlens is not None and cu_seqlens.dtype != torch.int32:
-        raise TypeError("cu_seqlens must be int32")
-    if sinks is not None and sinks.dtype != torch.float32:
-        raise TypeError("sinks must be float32")
+        _on_gpu(name, x, dev, torch.float32, contiguous=True, shape=(T, Hq))
+    if int(n_docs) > 0:
+        if cu_seqlens is None:
+            raise ValueError("cu_seqlens is required when n_docs > 0")
+        _on_gpu("cu_seqlens", cu_seqlens, dev, torch.int32, contiguous=True, min_numel=int(n_docs) + 1)
+    elif cu_seqlens is not None:
+        _on_gpu("cu_seqlens", cu_seqlens, dev, torch.int32, contiguous=True)
+    if sinks is not None:
+        _on_gpu("sinks", sinks, dev, torch.float32, contiguous=True, shape=(Hq,))
+        _on_gpu("dsinks", dsinks, dev, torch.float32, contiguous=True, shape=(Hq,))
     ds = [describe(x) for x in (q, k, v, out, dout, dq, dk, dv)]
     st = lib.varlen_attn_bwd(*(ctypes.byref(d) for d in ds[:5]), _ptr(lse), _ptr(cu_seqlens), int(n_docs),
                              int(window), float(scale), _ptr(sinks), *(ctypes.byref(d) for d in ds[5:]),
@@ -203,10 +255,12 @@ def sparse_mla_fwd(q: torch.Tensor, latent: torch.Tensor, k_pe: torch.Tensor, in
         out = torch.empty((T, H, Dl), dtype=q.dtype, device=q.device)
     if lse is None and return_lse:
         lse = torch.empty((T, H), dtype=torch.float32, device=q.device)
-    if doc_ids.dtype != torch.int32:
-        raise TypeError("doc_ids must be int32")
-    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != (T, H)):
-        raise ValueError("lse must be a contiguous float32 [T, H] tensor")
+    dev = _operand_device(q)
+    for name, x in (("latent", latent), ("k_pe", k_pe), ("indices", indices), ("out", out)):
+        _on_gpu(name, x, dev)
+    _on_gpu("doc_ids", doc_ids, dev, torch.int32, contiguous=True, shape=(T,))
+    if lse is not None:
+        _on_gpu("lse", lse, dev, torch.float32, contiguous=True, shape=(T, H))
     dq, dl, dr, di, do = describe(q), describe(latent), describe(k_pe), describe(indices), describe(out)
     st = lib.sparse_mla_fwd(ctypes.byref(dq), ctypes.byref(dl), ctypes.byref(dr), ctypes.byref(di),
                             _ptr(doc_ids), float(scale), ctypes.byref(do), _ptr(lse), _stream(stream))
@@ -226,6 +280,9 @@ def mla_value_proj(o_latent: torch.Tensor, value_weight: torch.Tensor, out: Opti
     Dv = value_weight.shape[1]
     if out is None:
         out = torch.empty((T, H, Dv), dtype=o_latent.dtype, device=o_latent.device)
+    dev = _operand_device(o_latent)
+    _on_gpu("value_weight", value_weight, dev)
+    _on_gpu("out", out, dev)
     do, dw, dout = describe(o_latent), describe(value_weight), describe(out)
     st = lib.mla_value_proj(ctypes.byref(do), ctypes.byref(dw), ctypes.byref(dout), _stream(stream))
     _check("mla_value_proj", st)
@@ -242,3 +299,36 @@ def sparse_mla(q: torch.Tensor, latent: torch.Tensor, k_pe: torch.Tensor, indice
     """
     o, lse = sparse_mla_fwd(q, latent, k_pe, indices, doc_ids, scale, stream=stream, return_lse=return_lse)
     return mla_value_proj(o, value_weight, stream=stream), lse
+
+
+# ------------------------------------------------------------- achievable-peak probes
+def peak_mfma_bf16(iters: int, sink: torch.Tensor, stream=None) -> float:
+    """Enqueue the bf16 MFMA-only loop (swa_peak_mfma_bf16); returns the flops it performs."""
+    lib = load_library()
+    _on_gpu("sink", sink, _operand_device(sink), torch.float32, min_numel=1)
+    _check("swa_peak_mfma_bf16", lib.swa_peak_mfma_bf16(_ptr(sink), int(iters), _stream(stream)))
+    return float(lib.swa_peak_mfma_bf16_flops(int(iters)))
+
+
+def peak_copy(src: torch.Tensor, dst: torch.Tensor, stream=None) -> int:
+    """Enqueue a streaming copy of src's bytes into dst; returns the bytes moved (read + write)."""
+    lib = load_library()
+    dev = _operand_device(src)
+    _on_gpu("src", src, dev, contiguous=True)
+    _on_gpu("dst", dst, dev, contiguous=True)
+    n = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < n:
+        raise ValueError("dst is smaller than src")
+    _check("swa_peak_copy", lib.swa_peak_copy(_ptr(src), _ptr(dst), n, _stream(stream)))
+    return 2 * n
+
+
+def peak_read(src: torch.Tensor, sink: torch.Tensor, stream=None) -> int:
+    """Enqueue a streaming read of src; returns the bytes read."""
+    lib = load_library()
+    dev = _operand_device(src)
+    _on_gpu("src", src, dev, contiguous=True)
+    _on_gpu("sink", sink, dev, torch.float32, min_numel=1)
+    n = src.numel() * src.element_size()
+    _check("swa_peak_read", lib.swa_peak_read(_ptr(src), n, _ptr(sink), _stream(stream)))
+    return n

@@ -50,44 +50,48 @@ struct Tile {
   bool padding;
 };
 
-// Decodes blockIdx into a tile; returns false for idle blocks.
-__device__ __forceinline__ bool decode_tile(const DenseFwdParams& p, Tile& w) {
-  // XCD-aware remap: workgroups reach the XCDs round-robin (x = blockIdx % 8, j = blockIdx / 8
-  // is the order within an XCD) and a head chunk's tiles stay on the XCDs whose L2 holds its
-  // K/V.  Under a full causal mask, when 8 / n_hc XCDs share a head chunk they deal its tiles
-  // round robin, so each gets the same mix of heavy and light tiles; otherwise (and for
-  // windows, whose tiles weigh about the same) each XCD takes a contiguous range.
+// Work item j of XCD x (the j-th item that XCD takes; per_xcd items each) -> head chunk hc and
+// virtual tile v.  Returns false past the end.  Workgroups reach the XCDs round-robin, and a
+// head chunk's tiles stay on the XCDs whose L2 holds its K/V.  Under a full causal mask, when
+// 8 / n_hc XCDs share a head chunk they deal its tiles round robin, so each gets the same mix
+// of heavy and light tiles; otherwise (and for windows, whose tiles weigh about the same) each
+// XCD takes a contiguous range.  Each document's tiles run last-first (heaviest first).
+__device__ __forceinline__ bool item_vtile(const DenseFwdParams& p, int x, int j, int per_xcd, int& hc, int& v) {
   const int VT = p.n_vtiles;
   const int n_hc = p.Hkv * p.n_chunks;
-  const int x = blockIdx.x % kXcds, j = blockIdx.x / kXcds;
-  int hc, r;
+  int r;
   if (p.window == 0 && n_hc < kXcds && kXcds % n_hc == 0) {
     const int m = kXcds / n_hc;
     hc = x % n_hc;
     r = j * m + x / n_hc;
     if (r >= VT) return false;
   } else {
-    const int L = x * (gridDim.x / kXcds) + j;
+    const int L = x * per_xcd + j;
     if (L >= p.n_work) return false;
     hc = L / VT;
     r = L - hc * VT;
   }
-  const int v = VT - 1 - r;  // each document's tiles last-first
+  v = VT - 1 - r;
+  return true;
+}
+
+// Virtual tile v of head chunk hc -> the workgroup's query tile; false for idle virtual tiles.
+// `bnd` is this lane's segment boundary bound(lane) when n_docs + 3 <= 64 (else unused).
+__device__ __forceinline__ bool vtile_to_tile(const DenseFwdParams& p, int hc, int v, int bnd, Tile& w) {
   w.g = hc / p.n_chunks;
   const int chunk = hc - w.g * p.n_chunks;
   const int TQ = p.tile_tokens;
   // segment s holding virtual tile v: A(s) = floor(bound(s) / TQ) + s, A(s) <= v < A(s+1).
   // A is increasing in s, so the segment is the number of s >= 1 with A(s) <= v: with at
-  // most 64 boundaries lane s loads bound(s) and one ballot counts them (one memory round
-  // trip); otherwise a binary search.
+  // most 64 boundaries lane s holds bound(s) and one ballot counts them; otherwise a binary
+  // search.
   int lo, seg_start, seg_end;
   if (p.n_docs + 3 <= 64) {  // lanes 0 .. n_docs + 2 hold every boundary
     const int s = threadIdx.x & 63;
-    const int b = seg_bound(p, s);
     lo = __builtin_amdgcn_readfirstlane(
-        __builtin_popcountll(__builtin_amdgcn_ballot_w64(s >= 1 && s <= p.n_docs + 1 && b < (v - s + 1) * TQ)));
-    seg_start = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_readlane(b, lo));
-    seg_end = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_readlane(b, lo + 1));
+        __builtin_popcountll(__builtin_amdgcn_ballot_w64(s >= 1 && s <= p.n_docs + 1 && bnd < (v - s + 1) * TQ)));
+    seg_start = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_readlane(bnd, lo));
+    seg_end = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_readlane(bnd, lo + 1));
   } else {
     lo = 0;
     int hi = p.n_docs + 2;
@@ -108,6 +112,14 @@ __device__ __forceinline__ bool decode_tile(const DenseFwdParams& p, Tile& w) {
   w.h0 = w.g * p.G + chunk * w.HB;
   w.padding = (lo == 0 || lo == p.n_docs + 1);
   return true;
+}
+
+// Decodes blockIdx into a tile (one tile per workgroup); returns false for idle blocks.
+__device__ __forceinline__ bool decode_tile(const DenseFwdParams& p, Tile& w) {
+  int hc, v;
+  if (!item_vtile(p, blockIdx.x % kXcds, blockIdx.x / kXcds, gridDim.x / kXcds, hc, v)) return false;
+  const int bnd = p.n_docs + 3 <= 64 ? seg_bound(p, threadIdx.x & 63) : 0;
+  return vtile_to_tile(p, hc, v, bnd, w);
 }
 
 // Per-lane query geometry inside the tile.

@@ -1,6 +1,7 @@
-"""The C ABI on the host: the library loads, exports what include/swattn.h declares,
+"""The C ABI on the host: the library loads, exports what include/*.h declare,
 and rejects every malformed call before touching the GPU (no compute call here)."""
 import ctypes
+import glob
 import math
 import os
 import re
@@ -13,16 +14,18 @@ from sliding_window_gqa_varlen_amd import binding
 from sliding_window_gqa_varlen_amd.binding import SwaError, describe
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "swattn.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 SWA_OK, SWA_ERR_NULL, SWA_ERR_DTYPE, SWA_ERR_SHAPE, SWA_ERR_ARG, SWA_ERR_UNSUPPORTED, SWA_ERR_LAYOUT = \
     0, -1, -2, -3, -4, -5, -6
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M))
+    return sorted(names)
 
 
 def test_header_declares_the_expected_entry_points():
@@ -134,10 +137,74 @@ def test_dense_empty_problem_is_a_no_op(lib):
     assert call_dense(lib, a, n_docs=0) == SWA_OK
 
 
-def test_binding_raises_with_the_library_detail(lib):
+def test_library_detail_reaches_swa_last_error(lib):
     a = dense_args()
-    with pytest.raises(SwaError, match="window"):
-        binding.varlen_attn_fwd(a["q"], a["k"], a["v"], a["cu"], window=-3, stream=0)
+    assert call_dense(lib, a, window=-3) == SWA_ERR_ARG
+    assert b"window" in lib.swa_last_error()
+
+
+def test_binding_refuses_host_tensors_before_any_call():
+    """A host tensor would give the kernel a host address: the binding refuses it."""
+    a = dense_args()
+    with pytest.raises(ValueError, match="GPU"):
+        binding.varlen_attn_fwd(a["q"], a["k"], a["v"], a["cu"], window=0, stream=0)
+    b = bwd_args()
+    with pytest.raises(ValueError, match="GPU"):
+        binding.varlen_attn_bwd(b["q"], b["k"], b["v"], b["out"], b["dout"], torch.zeros(16, 4), b["cu"], stream=0)
+    s = sparse_args()
+    with pytest.raises(ValueError, match="GPU"):
+        binding.sparse_mla_fwd(s["q"], s["latent"], s["k_pe"], s["idx"], s["ids"], stream=0)
+    v = vproj_args()
+    with pytest.raises(ValueError, match="GPU"):
+        binding.mla_value_proj(v["o"], v["w"], stream=0)
+    with pytest.raises(ValueError, match="GPU"):
+        binding.peak_copy(torch.zeros(16), torch.zeros(16), stream=0)
+
+
+class _FakeGpu(torch.Tensor):
+    """A host tensor that reports a GPU device, to drive the binding's size and layout checks
+    on a host without a GPU (they run before the library is called, so nothing reads it)."""
+
+    @staticmethod
+    def __new__(cls, t, device="cuda:0"):
+        r = torch.Tensor._make_subclass(cls, t)
+        r._fake_device = torch.device(device)
+        return r
+
+    @property
+    def device(self):
+        return self._fake_device
+
+
+def test_binding_size_and_layout_checks():
+    g = _FakeGpu
+    a = dense_args(T=16, Hq=4)
+    q, k, v, out = g(a["q"]), g(a["k"]), g(a["v"]), g(a["out"])
+    lse = g(torch.zeros(16, 4))
+    with pytest.raises(ValueError, match="cu_seqlens must hold at least 3"):
+        binding.varlen_attn_fwd(q, k, v, g(torch.tensor([0, 16], dtype=torch.int32)), n_docs=2, out=out, lse=lse,
+                                stream=0)
+    with pytest.raises(ValueError, match="cu_seqlens must be contiguous"):
+        binding.varlen_attn_fwd(q, k, v, g(torch.zeros(8, dtype=torch.int32)[::2]), n_docs=2, out=out, lse=lse,
+                                stream=0)
+    with pytest.raises(ValueError, match=r"sinks must have shape \(4,\)"):
+        binding.varlen_attn_fwd(q, k, v, g(a["cu"]), n_docs=1, sinks=g(torch.zeros(3)), out=out, lse=lse, stream=0)
+    with pytest.raises(ValueError, match="cu_seqlens is required"):
+        binding.varlen_attn_fwd(q, k, v, None, n_docs=1, out=out, lse=lse, stream=0)
+    with pytest.raises(ValueError, match="is on cuda:1"):
+        binding.varlen_attn_fwd(q, g(a["k"], "cuda:1"), v, g(a["cu"]), n_docs=1, out=out, lse=lse, stream=0)
+    with pytest.raises(ValueError, match=r"lse must have shape \(16, 4\)"):
+        binding.varlen_attn_fwd(q, k, v, g(a["cu"]), n_docs=1, out=out, lse=g(torch.zeros(16, 3)), stream=0)
+    b = {n: g(x) for n, x in bwd_args().items() if x is not None}
+    with pytest.raises(ValueError, match=r"dsinks must"):
+        binding.varlen_attn_bwd(b["q"], b["k"], b["v"], b["out"], b["dout"], g(torch.zeros(16, 4)), b["cu"], n_docs=1,
+                                sinks=g(torch.zeros(4)), dq=b["dq"], dk=b["dk"], dv=b["dv"], dsinks=g(torch.zeros(3)),
+                                delta=g(torch.zeros(16, 4)), stream=0)
+    sp = sparse_args(T=8)
+    with pytest.raises(ValueError, match=r"doc_ids must have shape \(8,\)"):
+        binding.sparse_mla_fwd(g(sp["q"]), g(sp["latent"]), g(sp["k_pe"]), g(sp["idx"]),
+                               g(torch.zeros(7, dtype=torch.int32)), out=g(sp["out"]), lse=g(torch.zeros(8, 16)),
+                               stream=0)
 
 
 # ---------------------------------------------------------------- sparse argument checks
@@ -249,7 +316,8 @@ def test_value_proj_rejects_output_aliasing_an_input(lib):
 def test_value_proj_empty_problem_is_a_no_op(lib):
     assert call_vproj(lib, vproj_args(T=0)) == SWA_OK
     a = vproj_args(T=0)
-    assert binding.mla_value_proj(a["o"], a["w"], stream=0).shape == (0, 4, 128)
+    with pytest.raises(ValueError, match="GPU"):  # the binding refuses host tensors even when empty
+        binding.mla_value_proj(a["o"], a["w"], stream=0)
 
 
 # ---------------------------------------------------------------- backward argument checks

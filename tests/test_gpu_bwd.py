@@ -5,12 +5,14 @@ forward's), the matching log-sum-exp and the same seeded dout; its dq, dk, dv, d
 compared element by element with the exact (fp64) gradients.
 
 Tolerance, per element, from the arithmetic of the kernel:
-  |got - ref| <= (2^-8 + 1e-4) |ref| + 6 * 2^-9 * rss + |e_delta| + 1e-6
-* 2^-8 |ref|: the one bf16 rounding of the result (round to nearest even, 8 significant
-  bits: relative error at most 2^-8).  1e-4 |ref| covers fp32 effects (exp2, accumulation
-  order, the fp32 lse).
+  |got - ref| <= (2^-8 + 1e-4) max(|ref|, |got|) + 6 * 2^-9 * rss + |e_delta| + 1e-6
+* 2^-8 max(|ref|, |got|): the one bf16 rounding of the result (round to nearest even, 8
+  significant bits: relative error at most 2^-8 of the value rounded, which is the exact
+  gradient shifted by e_delta).  1e-4 covers fp32 effects (exp2, accumulation order, the
+  fp32 lse).
 * 6 * 2^-9 * rss: rss is the root sum of squares of the terms the element sums (dv[j]:
-  P_ij dout[i]; dk[j]: scale dS_ij q[i]; dq[i]: scale dS_ij k[j]).  The kernel rounds P and
+  P_ij dout[i]; dk[j]: scale dS_ij q[i]; dq[i]: scale dS_ij k[j]), with the dS the kernel
+  forms from its delta (below).  The kernel rounds P and
   dS to bf16 as matrix operands; a rounding to 8 significant bits has a relative standard
   deviation of about 2^-9, independently per term, so the sum's error has a standard deviation
   of about 2^-9 rss; six of them bound it.  This matters where the terms cancel to a small
@@ -19,7 +21,11 @@ Tolerance, per element, from the arithmetic of the kernel:
   differs from the exact output (bf16 rounding, or the GPU forward's own error).  The
   gradient error this induces is linear and computed exactly by the test:
   dq_i: -scale (delta_used - delta)_i sum_j P_ij k_j ; dk_j: -scale sum_i P_ij (delta_used -
-  delta)_i q_i ; dv is unaffected.
+  delta)_i q_i ; dv is unaffected.  It also carries an fp32 bound: dP_ij and delta_i are fp32
+  sums of D products (error <= D 2^-24 of the sum of their magnitudes each) that cancel in
+  dS_ij = P_ij (dP_ij - delta_i) (exactly, on rows with one key), and P carries ~1e-6 of fp32
+  exp2 / lse error: |e| += scale sum_j (2 D 2^-24 + 1e-5) P_ij (|dout_i|.|v_j| + |dout_i|.|out_i|)
+  |k_j| for dq (likewise for dk), and 1e-5 sum_i P_ij |dout_i| for dv.
 
 dsinks_h = -sum_i p_sink_i delta_i is a sum whose terms cancel (delta_i = <dout_i, out_i> has
 either sign), so a relative bar does not apply.  Its error is set by the bf16 out the kernel
@@ -96,6 +102,7 @@ def term_rss(q, k, v, do, cu, window, scale, sinks, out_used=None):
     G = Hq // Hkv
     rq, rk, rv = np.zeros(q.shape), np.zeros(k.shape), np.zeros(v.shape)
     eq, ek = np.zeros(q.shape), np.zeros(k.shape)
+    fq, fk, fv = np.zeros(q.shape), np.zeros(k.shape), np.zeros(v.shape)
     for d in range(len(cu) - 1):
         s, e = int(cu[d]), int(cu[d + 1])
         for i0 in range(s, e, 256):  # query blocks; keys limited to the block's causal / window range
@@ -114,21 +121,31 @@ def term_rss(q, k, v, do, cu, window, scale, sinks, out_used=None):
                 P = E / Z[:, None]
                 dP = do[i0:i1, h] @ v[lo:i1, g].T
                 dS = P * (dP - (P * dP).sum(axis=1, keepdims=True))
-                rv[lo:i1, g] += (P ** 2).T @ do[i0:i1, h] ** 2
-                rk[lo:i1, g] += scale ** 2 * (dS ** 2).T @ q[i0:i1, h] ** 2
-                rq[i0:i1, h] = scale ** 2 * (dS ** 2) @ k[lo:i1, g] ** 2
+                # fp32 bound on the kernel's dS_ij = P_ij (dP_ij - delta_i): both dots are fp32
+                # sums of D products (relative error <= D 2^-24 of the sum of their magnitudes),
+                # and P carries ~1e-6 of fp32 exp2 / lse error
+                o_abs = np.abs(P @ v[lo:i1, g]) if out_used is None else np.abs(np.asarray(out_used[i0:i1, h], np.float64))
+                mag = np.abs(do[i0:i1, h]) @ np.abs(v[lo:i1, g]).T + (np.abs(do[i0:i1, h]) * o_abs).sum(axis=1)[:, None]
+                g32 = (2 * D * 2.0 ** -24 + 1e-5) * P * mag
+                fq[i0:i1, h] = scale * g32 @ np.abs(k[lo:i1, g])
+                fk[lo:i1, g] += scale * g32.T @ np.abs(q[i0:i1, h])
+                fv[lo:i1, g] += 1e-5 * P.T @ np.abs(do[i0:i1, h])
                 if out_used is not None:
                     o_exact = P @ v[lo:i1, g]
                     ddelta = (do[i0:i1, h] * (np.asarray(out_used[i0:i1, h], np.float64) - o_exact)).sum(axis=1)
                     eq[i0:i1, h] = -scale * ddelta[:, None] * (P @ k[lo:i1, g])
                     ek[lo:i1, g] += -scale * (P.T @ (ddelta[:, None] * q[i0:i1, h]))
-    return (np.sqrt(rq), np.sqrt(rk), np.sqrt(rv)), (np.abs(eq), np.abs(ek), np.zeros(v.shape))
+                    dS = dS - P * ddelta[:, None]  # the dS the kernel forms (and rounds) from that delta
+                rv[lo:i1, g] += (P ** 2).T @ do[i0:i1, h] ** 2
+                rk[lo:i1, g] += scale ** 2 * (dS ** 2).T @ q[i0:i1, h] ** 2
+                rq[i0:i1, h] = scale ** 2 * (dS ** 2) @ k[lo:i1, g] ** 2
+    return (np.sqrt(rq), np.sqrt(rk), np.sqrt(rv)), (np.abs(eq) + fq, np.abs(ek) + fk, fv)
 
 
 def check(got, ref, what, rss, e_delta=0.0):
     assert got.shape == ref.shape, what
     assert np.all(np.isfinite(got)), f"{what}: non-finite values"
-    bar = ROUND * np.abs(ref) + 6 * 2.0 ** -9 * rss + e_delta + 1e-6
+    bar = ROUND * np.maximum(np.abs(ref), np.abs(got)) + 6 * 2.0 ** -9 * rss + e_delta + 1e-6
     err = np.abs(got - ref) / bar
     i = np.unravel_index(np.argmax(err), err.shape)
     assert err.max() <= 1.0, f"{what}: error {err.max():.2f} x its bar at {i} (got {got[i]:.5f}, ref {ref[i]:.5f})"
