@@ -1,13 +1,20 @@
 #!/usr/bin/env python3
 """Benchmark of the packed varlen attention hot path on one MI355X.
 
-A step is one forward call over one batch of seeded synthetic input that is
-already resident in HBM.  Default workload: packed full-causal GQA forward,
-bf16, 8192 tokens in documents of 128..2048 tokens, 32 query / 8 KV heads,
-head_dim 128.  Prints one JSON line.
+A step is one forward call over one batch of seeded synthetic input that is already resident
+in HBM.  The headline workload (the line's `value`) is the packed full-causal GQA forward,
+bf16, 8192 tokens in documents of 128..2048 tokens, 32 query / 8 KV heads, head_dim 128.
+
+Default run: measured peaks (a bf16 MFMA-only loop, a streaming copy and read), then the
+sliding-window (1024), learned-sink window-128 and sparse MLA workloads, then the headline,
+each with W untimed warm-up steps and exactly K timed steps, back to back on the GPU; then
+the fp64 oracle on the host for each (time-capped).  One JSON line: the headline's fields at
+the top level, the other workloads under "configs", the probes under "measured_peaks".
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--no-cpu-baseline] [--copy-calibration MiB]
+
+--workload NAME times that one workload alone (profiling runs).
 """
 from __future__ import annotations
 
@@ -201,13 +208,226 @@ def cpu_baseline_vproj(inp, budget_s: float = 15.0) -> dict:
                       f"{t_total:.1f} s on {cpu_model()}"}
 
 
+SUITE = ("swa1024_gqa_bf16_t32768", "swa128_sink_gqa_bf16_t65536", "sparse_mla_bf16_t16384")
+HEADLINE = "causal_gqa_bf16_t8192"
+
+
+class Case:
+    """One workload prepared on the GPU: its step, its algorithmic work and how to price it."""
+
+    def __init__(self, wl, dev):
+        import torch
+        from sliding_window_gqa_varlen_amd import binding
+        self.wl = wl
+        self.kind = ("vproj" if isinstance(wl, W.ValueProjWorkload) else
+                     "sparse" if isinstance(wl, W.SparseWorkload) else
+                     "bwd" if getattr(wl, "backward", False) else "dense")
+        if self.kind == "vproj":
+            inp = W.make_value_proj(wl)
+            o_lat = torch.from_numpy(inp["o_latent"]).to(dev).to(torch.bfloat16)
+            vw = torch.from_numpy(inp["value_weight"]).to(dev).to(torch.bfloat16)
+            out = torch.empty(wl.T, wl.H, wl.d_value, device=dev, dtype=torch.bfloat16)
+            self.step = lambda: binding.mla_value_proj(o_lat, vw, out=out)
+            self.work = metrics.value_proj_bytes(wl.T, wl.H, wl.d_latent, wl.d_value)
+            self.flops = metrics.value_proj_flops(wl.T, wl.H, wl.d_latent, wl.d_value)
+            self.sources, self.dtype = VPROJ_SOURCES, "bf16"
+            self.config = {"workload": wl.name, "tokens": wl.T, "heads": wl.H, "d_latent": wl.d_latent,
+                           "d_value": wl.d_value}
+        elif self.kind == "bwd":
+            inp = W.make_dense(wl)
+            q, k, v = (torch.from_numpy(inp[n]).to(dev).to(torch.bfloat16) for n in ("q", "k", "v"))
+            cu = torch.from_numpy(inp["cu_seqlens"]).to(dev)
+            sinks = None if inp["sinks"] is None else torch.from_numpy(inp["sinks"]).to(dev)
+            o_fwd, lse = binding.varlen_attn_fwd(q, k, v, cu, inp["n_docs"], wl.window, wl.scale, sinks)
+            dout = torch.from_numpy(W.make_dout(wl.seed, inp["q"].shape)).to(dev).to(torch.bfloat16)
+            dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+            delta = torch.empty(wl.T, wl.Hq, device=dev, dtype=torch.float32)
+            dsinks = None if sinks is None else torch.empty(wl.Hq, device=dev, dtype=torch.float32)
+            self.step = lambda: binding.varlen_attn_bwd(q, k, v, o_fwd, dout, lse, cu, inp["n_docs"], wl.window,
+                                                        wl.scale, sinks, dq=dq, dk=dk, dv=dv, dsinks=dsinks,
+                                                        delta=delta)
+            self.flops = self.work = metrics.dense_bwd_flops(inp["lengths"], wl.window, wl.Hq, wl.D)
+            self.min_bytes = metrics.dense_bwd_min_bytes(wl.T, wl.Hq, wl.Hkv, wl.D, inp["n_docs"], wl.sinks)
+            self.sources, self.dtype = BWD_SOURCES, "bf16"
+            self.config = {"workload": wl.name, "tokens": wl.T, "documents": inp["n_docs"], "q_heads": wl.Hq,
+                           "kv_heads": wl.Hkv, "head_dim": wl.D, "window": wl.window, "sinks": wl.sinks,
+                           "allowed_pairs": metrics.dense_allowed_pairs(inp["lengths"], wl.window),
+                           "kernels": "delta, dq, dk/dv (one varlen_attn_bwd call)"}
+        elif self.kind == "sparse":
+            inp = W.make_sparse(wl)
+            q = torch.from_numpy(inp["q"]).to(dev).to(torch.bfloat16)
+            lat = torch.from_numpy(inp["latent"]).to(dev).to(torch.bfloat16)
+            kpe = torch.from_numpy(inp["k_pe"]).to(dev).to(torch.bfloat16)
+            idx = torch.from_numpy(inp["indices"]).to(dev)
+            ids = torch.from_numpy(inp["doc_ids"]).to(dev)
+            out = torch.empty(wl.T, wl.H, wl.d_latent, device=dev, dtype=torch.bfloat16)
+            lse = torch.empty(wl.T, wl.H, device=dev, dtype=torch.float32)
+            self.step = lambda: binding.sparse_mla_fwd(q, lat, kpe, idx, ids, wl.scale, out=out, lse=lse)
+            valid = metrics.sparse_valid_slots(inp["indices"], inp["doc_ids"])
+            self.work = metrics.sparse_bytes(valid, wl.T, wl.H, wl.d_latent, wl.d_rope, wl.topk)
+            self.flops = metrics.sparse_flops(valid, wl.H, wl.d_latent, wl.d_rope)
+            self.sources, self.dtype = SPARSE_SOURCES, "bf16"
+            self.config = {"workload": wl.name, "tokens": wl.T, "heads": wl.H, "d_latent": wl.d_latent,
+                           "d_rope": wl.d_rope, "topk": wl.topk, "valid_slots": valid,
+                           "documents": len(inp["lengths"])}
+        else:
+            inp = W.make_dense(wl)
+            td = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+            q, k, v = (torch.from_numpy(inp[n]).to(dev).to(td) for n in ("q", "k", "v"))
+            cu = torch.from_numpy(inp["cu_seqlens"]).to(dev)
+            sinks = None if inp["sinks"] is None else torch.from_numpy(inp["sinks"]).to(dev)
+            out = torch.empty(wl.T, wl.Hq, wl.D, device=dev, dtype=td)
+            lse = torch.empty(wl.T, wl.Hq, device=dev, dtype=torch.float32)
+            self.step = lambda: binding.varlen_attn_fwd(q, k, v, cu, inp["n_docs"], wl.window, wl.scale, sinks,
+                                                        out=out, lse=lse)
+            self.flops = self.work = metrics.dense_flops(inp["lengths"], wl.window, wl.Hq, wl.D)
+            self.min_bytes = metrics.dense_min_bytes(wl.T, wl.Hq, wl.Hkv, wl.D, 2 if wl.dtype == "bf16" else 4,
+                                                     inp["n_docs"], True, wl.sinks)
+            self.sources, self.dtype = DENSE_SOURCES, wl.dtype
+            self.config = {"workload": wl.name, "tokens": wl.T, "documents": inp["n_docs"], "q_heads": wl.Hq,
+                           "kv_heads": wl.Hkv, "head_dim": wl.D, "window": wl.window, "sinks": wl.sinks,
+                           "allowed_pairs": metrics.dense_allowed_pairs(inp["lengths"], wl.window)}
+        inp["workload"] = wl
+        self.inp = inp
+        self.ms = None
+
+    def timed(self, warmup: int, steps: int) -> float:
+        """W untimed steps, then exactly K steps between HIP events on the launch stream; ms per step."""
+        import torch
+        torch.cuda.synchronize()
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()  # the library launches on this stream
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        for _ in range(steps):
+            self.step()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        self.ms = ev0.elapsed_time(ev1) / max(steps, 1)
+        return self.ms
+
+    def launch_spread(self, n: int = 20) -> dict:
+        """Individually timed launches (a separate pass, not part of `value`)."""
+        import torch
+        stream = torch.cuda.current_stream()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for a, b in evs:
+            a.record(stream)
+            self.step()
+            b.record(stream)
+        torch.cuda.synchronize()
+        per = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
+        return {"median": per[len(per) // 2], "min": per[0], "max": per[-1], "launches": len(per)}
+
+    def cold_us(self, dev) -> float:
+        """Sparse: median of 5 launches, each after a 512 MiB device write that evicts the key table."""
+        import torch
+        stream = torch.cuda.current_stream()
+        flush = torch.empty(512 << 20, device=dev, dtype=torch.uint8)
+        cold = []
+        for _ in range(5):
+            flush.fill_(1)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            self.step()
+            b.record(stream)
+            torch.cuda.synchronize()
+            cold.append(a.elapsed_time(b) * 1e3)
+        del flush
+        return sorted(cold)[len(cold) // 2]
+
+    def result(self, peaks: dict | None) -> dict:
+        """metric, value, unit, roofline (against the published peak, with the measured one beside it)."""
+        wl, ms = self.wl, self.ms
+        traffic = committed_traffic(wl.name, self.sources)
+        cfg = dict(self.config)
+        mfma_meas = (peaks or {}).get("bf16_mfma_tflops")
+        hbm_meas = (peaks or {}).get("copy_gbps")
+        if self.kind in ("vproj", "sparse"):
+            achieved = self.work / (ms * 1e-3) / 1e9
+            roof = metrics.roofline("hbm", achieved, metrics.MI355X_HBM_GBPS, "GB/s", traffic)
+            roof["measured_peak"] = hbm_meas
+            cfg["tflops"] = self.flops / (ms * 1e-3) / 1e12
+            metric = ("sparse MLA value up-projection algorithmic HBM GB/s (1 GPU)" if self.kind == "vproj" else
+                      "sparse MLA fwd algorithmic HBM GB/s (1 GPU)")
+            unit = "GB/s"
+        else:
+            achieved = self.flops / (ms * 1e-3) / 1e12
+            bf16 = self.dtype == "bf16"
+            peak = metrics.MI355X_BF16_DENSE_TFLOPS if bf16 else metrics.MI355X_FP32_MFMA_TFLOPS
+            hbm_gbps = self.min_bytes / (ms * 1e-3) / 1e9
+            # the roofline that binds: HBM when the arithmetic intensity is below the ridge point
+            if self.flops / self.min_bytes < peak * 1e12 / (metrics.MI355X_HBM_GBPS * 1e9):
+                roof = metrics.roofline("hbm", hbm_gbps, metrics.MI355X_HBM_GBPS, "GB/s", traffic)
+                roof["measured_peak"] = hbm_meas
+            else:
+                roof = metrics.roofline("mfma", achieved, peak, "TFLOP/s", traffic)
+                roof["measured_peak"] = mfma_meas if bf16 else None
+            cfg["pct_bf16_mfma_peak"] = 100.0 * achieved / metrics.MI355X_BF16_DENSE_TFLOPS
+            cfg["min_hbm_gbps"] = hbm_gbps
+            cfg["arithmetic_intensity"] = self.flops / self.min_bytes
+            metric = ("packed GQA attn bwd mask-effective TFLOP/s + % bf16 MFMA peak (1 GPU)" if self.kind == "bwd"
+                      else "packed GQA attn fwd mask-effective TFLOP/s + % bf16 MFMA peak (1 GPU)")
+            unit = "TFLOP/s"
+        if roof.get("measured_peak"):
+            roof["frac_of_measured_peak"] = roof["achieved"] / roof["measured_peak"]
+        return {"metric": metric, "value": achieved, "unit": unit, "ms_per_step": ms, "dtype": self.dtype,
+                "config": cfg, "roofline": roof}
+
+    def cpu_baseline(self, budget_s: float) -> dict:
+        if self.kind == "vproj":
+            return cpu_baseline_vproj(self.inp, budget_s=budget_s)
+        if self.kind == "sparse":
+            return cpu_baseline_sparse(self.inp, budget_s=budget_s)
+        if self.kind == "bwd":
+            return cpu_baseline_dense_bwd(self.inp, min_s=budget_s, max_s=3 * budget_s)
+        return cpu_baseline_dense(self.inp, min_s=budget_s, max_s=3 * budget_s)
+
+
+def measure_peaks(dev) -> dict:
+    """Achievable peaks of this device from the library's probes (median of 5 launches each)."""
+    import torch
+    from sliding_window_gqa_varlen_amd import binding
+    stream = torch.cuda.current_stream()
+    sink = torch.zeros(1, device=dev, dtype=torch.float32)
+
+    def time_it(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        out = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            amount = fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            out.append(amount / (a.elapsed_time(b) * 1e-3))
+        return sorted(out)[len(out) // 2], max(out)
+
+    mfma, mfma_max = time_it(lambda: binding.peak_mfma_bf16(4000, sink))
+    buf = torch.empty(2, 1 << 28, device=dev, dtype=torch.float32)  # two 1 GiB halves
+    buf.fill_(1.0)
+    copy, copy_max = time_it(lambda: binding.peak_copy(buf[0], buf[1]))
+    read, read_max = time_it(lambda: binding.peak_read(buf[0], sink))
+    del buf
+    return {"bf16_mfma_tflops": mfma / 1e12, "bf16_mfma_tflops_max": mfma_max / 1e12,
+            "copy_gbps": copy / 1e9, "copy_gbps_max": copy_max / 1e9,
+            "read_gbps": read / 1e9, "read_gbps_max": read_max / 1e9,
+            "spec_bf16_mfma_tflops": metrics.MI355X_BF16_DENSE_TFLOPS, "spec_hbm_gbps": metrics.MI355X_HBM_GBPS,
+            "note": "median of 5 launches of swa_peak_mfma_bf16 (MFMA-only loop, 8 waves per CU), swa_peak_copy "
+                    "(1 GiB -> 1 GiB, read + write bytes) and swa_peak_read (1 GiB)"}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", default="causal_gqa_bf16_t8192",
-                    choices=[w.name for w in W.WORKLOADS + W.EXTRA_WORKLOADS])
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=None,
+                    choices=[w.name for w in W.WORKLOADS + W.EXTRA_WORKLOADS],
+                    help="time this workload alone (default: the headline plus the suite)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after the timed steps, run a plain device copy of this many MiB (counter calibration)")
@@ -222,130 +442,21 @@ def main() -> int:
 
     binding.load_library()  # raises when the HIP library is missing: there is no fallback path
     dev = torch.device("cuda:0")
-    wl = next(w for w in W.WORKLOADS + W.EXTRA_WORKLOADS if w.name == args.workload)
-    sparse = isinstance(wl, W.SparseWorkload)
-    vproj = isinstance(wl, W.ValueProjWorkload)
+    by_name = {w.name: w for w in W.WORKLOADS + W.EXTRA_WORKLOADS}
+    suite = args.workload is None
+    head_name = HEADLINE if suite else args.workload
 
-    if vproj:
-        inp = W.make_value_proj(wl)
-        o_lat = torch.from_numpy(inp["o_latent"]).to(dev).to(torch.bfloat16)
-        vw = torch.from_numpy(inp["value_weight"]).to(dev).to(torch.bfloat16)
-        out = torch.empty(wl.T, wl.H, wl.d_value, device=dev, dtype=torch.bfloat16)
-
-        def step():
-            binding.mla_value_proj(o_lat, vw, out=out)
-
-        work = metrics.value_proj_bytes(wl.T, wl.H, wl.d_latent, wl.d_value)
-        flops = metrics.value_proj_flops(wl.T, wl.H, wl.d_latent, wl.d_value)
-        sources = VPROJ_SOURCES
-        dtype = "bf16"
-        config = {"workload": wl.name, "tokens": wl.T, "heads": wl.H, "d_latent": wl.d_latent,
-                  "d_value": wl.d_value}
-    elif getattr(wl, "backward", False):
-        inp = W.make_dense(wl)
-        q, k, v = (torch.from_numpy(inp[n]).to(dev).to(torch.bfloat16) for n in ("q", "k", "v"))
-        cu = torch.from_numpy(inp["cu_seqlens"]).to(dev)
-        sinks = None if inp["sinks"] is None else torch.from_numpy(inp["sinks"]).to(dev)
-        o_fwd, lse = binding.varlen_attn_fwd(q, k, v, cu, inp["n_docs"], wl.window, wl.scale, sinks)
-        dout = torch.from_numpy(W.make_dout(wl.seed, inp["q"].shape)).to(dev).to(torch.bfloat16)
-        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-        delta = torch.empty(wl.T, wl.Hq, device=dev, dtype=torch.float32)
-        dsinks = None if sinks is None else torch.empty(wl.Hq, device=dev, dtype=torch.float32)
-
-        def step():
-            binding.varlen_attn_bwd(q, k, v, o_fwd, dout, lse, cu, inp["n_docs"], wl.window, wl.scale, sinks,
-                                    dq=dq, dk=dk, dv=dv, dsinks=dsinks, delta=delta)
-
-        flops = metrics.dense_bwd_flops(inp["lengths"], wl.window, wl.Hq, wl.D)
-        work = flops
-        sources = BWD_SOURCES
-        dtype = "bf16"
-        config = {"workload": wl.name, "tokens": wl.T, "documents": inp["n_docs"], "q_heads": wl.Hq,
-                  "kv_heads": wl.Hkv, "head_dim": wl.D, "window": wl.window, "sinks": wl.sinks,
-                  "allowed_pairs": metrics.dense_allowed_pairs(inp["lengths"], wl.window),
-                  "kernels": "delta, dq, dk/dv (one varlen_attn_bwd call)"}
-    elif sparse:
-        inp = W.make_sparse(wl)
-        q = torch.from_numpy(inp["q"]).to(dev).to(torch.bfloat16)
-        lat = torch.from_numpy(inp["latent"]).to(dev).to(torch.bfloat16)
-        kpe = torch.from_numpy(inp["k_pe"]).to(dev).to(torch.bfloat16)
-        idx = torch.from_numpy(inp["indices"]).to(dev)
-        ids = torch.from_numpy(inp["doc_ids"]).to(dev)
-        out = torch.empty(wl.T, wl.H, wl.d_latent, device=dev, dtype=torch.bfloat16)
-        lse = torch.empty(wl.T, wl.H, device=dev, dtype=torch.float32)
-
-        def step():
-            binding.sparse_mla_fwd(q, lat, kpe, idx, ids, wl.scale, out=out, lse=lse)
-
-        valid = metrics.sparse_valid_slots(inp["indices"], inp["doc_ids"])
-        work = metrics.sparse_bytes(valid, wl.T, wl.H, wl.d_latent, wl.d_rope, wl.topk)
-        flops = metrics.sparse_flops(valid, wl.H, wl.d_latent, wl.d_rope)
-        sources = SPARSE_SOURCES
-        dtype = "bf16"
-        config = {"workload": wl.name, "tokens": wl.T, "heads": wl.H, "d_latent": wl.d_latent,
-                  "d_rope": wl.d_rope, "topk": wl.topk, "valid_slots": valid, "documents": len(inp["lengths"])}
-    else:
-        inp = W.make_dense(wl)
-        td = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
-        q = torch.from_numpy(inp["q"]).to(dev).to(td)
-        k = torch.from_numpy(inp["k"]).to(dev).to(td)
-        v = torch.from_numpy(inp["v"]).to(dev).to(td)
-        cu = torch.from_numpy(inp["cu_seqlens"]).to(dev)
-        sinks = None if inp["sinks"] is None else torch.from_numpy(inp["sinks"]).to(dev)
-        out = torch.empty(wl.T, wl.Hq, wl.D, device=dev, dtype=td)
-        lse = torch.empty(wl.T, wl.Hq, device=dev, dtype=torch.float32)
-
-        def step():
-            binding.varlen_attn_fwd(q, k, v, cu, inp["n_docs"], wl.window, wl.scale, sinks, out=out, lse=lse)
-
-        flops = metrics.dense_flops(inp["lengths"], wl.window, wl.Hq, wl.D)
-        work = flops
-        sources = DENSE_SOURCES
-        dtype = wl.dtype
-        config = {"workload": wl.name, "tokens": wl.T, "documents": inp["n_docs"], "q_heads": wl.Hq,
-                  "kv_heads": wl.Hkv, "head_dim": wl.D, "window": wl.window, "sinks": wl.sinks,
-                  "allowed_pairs": metrics.dense_allowed_pairs(inp["lengths"], wl.window)}
-
+    # inputs first (host work), so the GPU measurements below run back to back
+    head = Case(by_name[head_name], dev)
+    others = [Case(by_name[n], dev) for n in SUITE] if suite else []
     torch.cuda.synchronize()
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()  # the library launches on this stream
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    ev0.record(stream)
-    for _ in range(args.steps):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    ms = ev0.elapsed_time(ev1) / max(args.steps, 1)
 
-    # per-launch spread: a separate pass of individually timed launches (not part of `value`)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
-    for a, b in evs:
-        a.record(stream)
-        step()
-        b.record(stream)
-    torch.cuda.synchronize()
-    per = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
-    launch_us = {"median": per[len(per) // 2], "min": per[0], "max": per[-1], "launches": len(per)}
-
-    # sparse: the 18.9 MB key table otherwise stays in the Infinity Cache between launches; a
-    # cold launch follows a 512 MiB write that evicts it (separate pass, not part of `value`)
-    cold_us = None
-    if sparse:
-        flush = torch.empty(512 << 20, device=dev, dtype=torch.uint8)
-        cold = []
-        for _ in range(5):
-            flush.fill_(1)
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            step()
-            b.record(stream)
-            torch.cuda.synchronize()
-            cold.append(a.elapsed_time(b) * 1e3)
-        del flush
-        cold_us = sorted(cold)[len(cold) // 2]
+    peaks = measure_peaks(dev) if suite else None
+    for c in others:
+        c.timed(args.warmup, args.steps)
+    head.timed(args.warmup, args.steps)
+    spread = head.launch_spread()
+    cold = head.cold_us(dev) if head.kind == "sparse" else None
 
     if args.copy_calibration > 0:
         n = args.copy_calibration * (1 << 20) // 4
@@ -356,65 +467,26 @@ def main() -> int:
         torch.cuda.synchronize()
         del a, b
 
-    traffic = committed_traffic(wl.name, sources)
-    if vproj:
-        achieved = work / (ms * 1e-3) / 1e9
-        value = achieved
-        roof = metrics.roofline("hbm", achieved, metrics.MI355X_HBM_GBPS, "GB/s", traffic)
-        metric, unit = "sparse MLA value up-projection algorithmic HBM GB/s (1 GPU)", "GB/s"
-    elif getattr(wl, "backward", False):
-        achieved = flops / (ms * 1e-3) / 1e12
-        value = achieved
-        min_bytes = metrics.dense_bwd_min_bytes(wl.T, wl.Hq, wl.Hkv, wl.D, inp["n_docs"], wl.sinks)
-        hbm_gbps = min_bytes / (ms * 1e-3) / 1e9
-        # the roofline that binds, as for the forward
-        if flops / min_bytes < metrics.MI355X_BF16_DENSE_TFLOPS * 1e12 / (metrics.MI355X_HBM_GBPS * 1e9):
-            roof = metrics.roofline("hbm", hbm_gbps, metrics.MI355X_HBM_GBPS, "GB/s", traffic)
-        else:
-            roof = metrics.roofline("mfma", achieved, metrics.MI355X_BF16_DENSE_TFLOPS, "TFLOP/s", traffic)
-        metric, unit = "packed GQA attn bwd mask-effective TFLOP/s + % bf16 MFMA peak (1 GPU)", "TFLOP/s"
-        config["pct_bf16_mfma_peak"] = 100.0 * achieved / metrics.MI355X_BF16_DENSE_TFLOPS
-        config["min_hbm_gbps"] = hbm_gbps
-        config["arithmetic_intensity"] = flops / min_bytes
-    elif sparse:
-        achieved = work / (ms * 1e-3) / 1e9
-        value = achieved
-        roof = metrics.roofline("hbm", achieved, metrics.MI355X_HBM_GBPS, "GB/s", traffic)
-        metric, unit = "sparse MLA fwd algorithmic HBM GB/s (1 GPU)", "GB/s"
-    else:
-        achieved = flops / (ms * 1e-3) / 1e12
-        value = achieved
-        peak = metrics.MI355X_BF16_DENSE_TFLOPS if wl.dtype == "bf16" else metrics.MI355X_FP32_MFMA_TFLOPS
-        min_bytes = metrics.dense_min_bytes(wl.T, wl.Hq, wl.Hkv, wl.D, 2 if wl.dtype == "bf16" else 4,
-                                            inp["n_docs"], True, wl.sinks)
-        hbm_gbps = min_bytes / (ms * 1e-3) / 1e9
-        # the roofline that binds: HBM when the arithmetic intensity is below the ridge point
-        if flops / min_bytes < peak * 1e12 / (metrics.MI355X_HBM_GBPS * 1e9):
-            roof = metrics.roofline("hbm", hbm_gbps, metrics.MI355X_HBM_GBPS, "GB/s", traffic)
-        else:
-            roof = metrics.roofline("mfma", achieved, peak, "TFLOP/s", traffic)
-        metric, unit = "packed GQA attn fwd mask-effective TFLOP/s + % bf16 MFMA peak (1 GPU)", "TFLOP/s"
-        config["pct_bf16_mfma_peak"] = 100.0 * achieved / metrics.MI355X_BF16_DENSE_TFLOPS
-        config["min_hbm_gbps"] = hbm_gbps
-        config["arithmetic_intensity"] = flops / min_bytes
+    r = head.result(peaks)
     line = {
-        "metric": metric, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": dtype, "data": "synthetic (seeded generator, inputs resident in HBM)",
-        "config": config, "roofline": roof,
-        "cpu_baseline": None,
+        "metric": r["metric"], "value": r["value"], "unit": r["unit"], "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": r["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": r["dtype"], "data": "synthetic (seeded generator, inputs resident in HBM)",
+        "config": r["config"], "roofline": r["roofline"], "cpu_baseline": None,
     }
-    if sparse or vproj:
-        line["config"]["tflops"] = flops / (ms * 1e-3) / 1e12
-    line["launch_us"] = launch_us
-    if cold_us is not None:
-        line["cold"] = {"us": cold_us, "value": work / (cold_us * 1e-6) / 1e9, "unit": unit,
+    line["launch_us"] = spread
+    if cold is not None:
+        line["cold"] = {"us": cold, "value": head.work / (cold * 1e-6) / 1e9, "unit": r["unit"],
                         "note": "median of 5 launches, each after a 512 MiB device write that evicts the key table"}
+    if suite:
+        line["configs"] = {c.wl.name: c.result(peaks) for c in others}
+        line["measured_peaks"] = peaks
+        line["order"] = ("probes, then " + ", ".join(SUITE) + ", then the headline, each W warm-up + K timed "
+                         "steps back to back on the GPU; oracle baselines on the host afterwards")
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = (cpu_baseline_vproj(inp) if vproj else
-                                cpu_baseline_sparse(inp) if sparse else
-                                cpu_baseline_dense_bwd(inp) if getattr(wl, "backward", False) else
-                                cpu_baseline_dense(inp))
+        line["cpu_baseline"] = head.cpu_baseline(10.0)
+        for c in others:
+            line["configs"][c.wl.name]["cpu_baseline"] = c.cpu_baseline(6.0)
     print(json.dumps(line), flush=True)
     return 0
 
