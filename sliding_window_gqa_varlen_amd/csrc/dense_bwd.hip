@@ -44,15 +44,9 @@ namespace swa {
 namespace {
 
 constexpr int kTK = 128;           // keys per dk/dv workgroup
-#ifndef SWA_BWD_AHEAD
-#define SWA_BWD_AHEAD 8
-#endif
-#ifndef SWA_DQ_OCC64
-#define SWA_DQ_OCC64 3  // head_dim 64 dq: 3 waves / SIMD (168 VGPRs, 2 dwords spilled outside the loop)
-#endif
-#ifndef SWA_BWD_AHEAD64
-#define SWA_BWD_AHEAD64 4
-#endif
+constexpr int kBwdAhead = 8;    // dk/dv operand fragments read this many MFMAs ahead (head_dim 128)
+constexpr int kBwdAhead64 = 4;  // the same for head_dim 64
+constexpr int kDqOcc64 = 3;     // head_dim 64 dq: 3 waves / SIMD (168 VGPRs, 2 dwords spilled outside the loop)
 
 template <int D>
 struct Bw {
@@ -206,7 +200,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dsink_reduce_kernel(DenseBwdPara
 // dq: query-parallel, the forward's tiles
 // ======================================================================================
 template <int D>
-__global__ __launch_bounds__(kThreads, D == 64 ? SWA_DQ_OCC64 : 2) void bwd_dq_kernel(DenseBwdParams p) {
+__global__ __launch_bounds__(kThreads, D == 64 ? kDqOcc64 : 2) void bwd_dq_kernel(DenseBwdParams p) {
   using B = Bw<D>;
   __shared__ u32x4 k0[B::TileUnits];
   __shared__ u32x4 k1[B::TileUnits];
@@ -466,7 +460,7 @@ __device__ __forceinline__ void dkdv_tile(const u32x4* qb, const u32x4* ob, cons
   constexpr int NS = B::NS, NV = B::NV, NF = 2 * NS + 2 * NV;
   constexpr int EPS = 32 / NS;  // probabilities per dP slot
   constexpr int DPS = 32 / NV;  // dS elements per dV slot
-  constexpr int kAhead = D == 64 ? SWA_BWD_AHEAD64 : SWA_BWD_AHEAD;
+  constexpr int kAhead = D == 64 ? kBwdAhead64 : kBwdAhead;
   static_assert(32 % NS == 0 && 32 % NV == 0 && NS >= 8, "slot shares");
   bf16x8 frag[NF];
   auto read = [&](int f) {
@@ -716,7 +710,7 @@ __device__ __forceinline__ void dkdv16_tile(const u32x4* qb, const u32x4* ob, co
                                             const bf16x8 (&kf)[4], const bf16x8 (&vf)[4], int raddr,
                                             const int (&toff)[8], float c2, f32x4 (&dk)[8], f32x4 (&dv)[8],
                                             int qoff, int eoff, int W, int g) {
-  constexpr int kAhead = SWA_BWD_AHEAD;
+  constexpr int kAhead = kBwdAhead;
   bf16x8 frag[64];
   auto read = [&](int f) {
     if (f < 32) {  // S (f < 16) or dP: query block b = f & 3, k-step s = (f >> 2) & 3

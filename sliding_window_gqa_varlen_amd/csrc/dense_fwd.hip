@@ -47,15 +47,9 @@ namespace swa {
 namespace {
 
 constexpr float kRescaleLog2 = 8.f;  // lazy-rescale threshold (log2 units)
-#ifndef SWA_KAHEAD128
-#define SWA_KAHEAD128 8
-#endif
-#ifndef SWA_KAHEAD64
-#define SWA_KAHEAD64 4
-#endif
-#ifndef SWA_OCC64
-#define SWA_OCC64 3
-#endif
+constexpr int kAhead128 = 8;  // operand fragments read this many MFMAs ahead (head_dim >= 128)
+constexpr int kAhead64 = 4;   // the same for head_dim 64
+constexpr int kOcc64 = 3;     // head_dim 64: three workgroups per CU
 
 template <typename T, int D>
 __device__ __forceinline__ void write_padding(const DenseFwdParams& p, const Tile& w) {
@@ -355,7 +349,7 @@ __device__ __forceinline__ float qk_pv_step(const u32x4* kbuf, const u32x4* vbuf
   constexpr int NQ = 2 * B::kQFrags;  // QK^T MFMAs (32 for D = 256, 16 for D = 128, 8 for D = 64)
   constexpr int NP = 4 * B::kDBlocks; // PV MFMAs
   constexpr int EPM = 32 / NQ;        // exponentials per QK^T MFMA slot
-  constexpr int kAhead = (D >= 128) ? SWA_KAHEAD128 : SWA_KAHEAD64;
+  constexpr int kAhead = (D >= 128) ? kAhead128 : kAhead64;
   static_assert(32 % NQ == 0, "the 32 exponentials split evenly over the QK^T slots");
   u32x4 frag[NQ + NP];
   __builtin_amdgcn_s_setprio(1);  // the wave in its MFMA stream goes first
@@ -418,7 +412,7 @@ __device__ __forceinline__ float qk_pv_step(const u32x4* kbuf, const u32x4* vbuf
 }
 
 template <int D>
-__global__ __launch_bounds__(kThreads, D == 64 ? SWA_OCC64 : D == 128 ? 2 : 1) void dense_fwd_bf16_kernel(
+__global__ __launch_bounds__(kThreads, D == 64 ? kOcc64 : D == 128 ? 2 : 1) void dense_fwd_bf16_kernel(
     DenseFwdParams p) {
   using B = Bf<D>;
   __shared__ u32x4 k0[B::kTileUnits];

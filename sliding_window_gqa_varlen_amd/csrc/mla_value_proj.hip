@@ -18,9 +18,6 @@
 #include "device_common.h"
 #include "launch.h"
 
-#ifndef SWA_VPROJ_SLOTS128
-#define SWA_VPROJ_SLOTS128 4
-#endif
 
 namespace swa {
 namespace {
@@ -52,7 +49,7 @@ __device__ __forceinline__ void barrier_keep_loads() {
 template <int DV>
 __global__ __launch_bounds__(kThreads, 1) void mla_value_proj_kernel(MlaValueProjParams p) {
   constexpr int MB = DV / 32;           // 32-row blocks of W
-  constexpr int kSlots = DV == 128 ? SWA_VPROJ_SLOTS128 : 4;  // ring of 32 KiB slots
+  constexpr int kSlots = 4;  // ring of 32 KiB slots
   constexpr int P = kWaves / MB;        // slots consumed per iteration
   constexpr int kAhead = kSlots / P - 1;  // iterations loaded ahead
   constexpr int kIterTokens = kTile * P;

@@ -28,12 +28,6 @@
 #include "device_common.h"
 #include "launch.h"
 
-#ifndef SWA_SPARSE_QAHEAD
-#define SWA_SPARSE_QAHEAD 3
-#endif
-#ifndef SWA_SPARSE_PVAHEAD
-#define SWA_SPARSE_PVAHEAD 2
-#endif
 
 namespace swa {
 namespace {
@@ -57,8 +51,8 @@ constexpr int kTokenRun = 64;                       // consecutive tokens per XC
 constexpr int kSlotsPerThread = kSeg / kThreads;    // 4
 constexpr int kDBlocks = 8;                         // 256 output coordinates per wave / 32
 constexpr float kRescaleLog2 = 8.f;                 // lazy-rescale threshold (log2 units)
-constexpr int kQAhead = SWA_SPARSE_QAHEAD;          // QK^T fragments read ahead of their MFMA
-constexpr int kPvAhead = SWA_SPARSE_PVAHEAD;        // PV fragments read ahead of their MFMA
+constexpr int kQAhead = 3;         // QK^T fragments read ahead of their MFMA
+constexpr int kPvAhead = 2;       // PV fragments read ahead of their MFMA
 static_assert(kLatRegion % (64 * kWaves) == 0 && (kSlots * kRopeUnits * 4) % (64 * kWaves) == 0,
               "every wave issues the same number of gathers");
 
