@@ -191,21 +191,20 @@ __device__ __forceinline__ f32x16 qk_partial(const u32x4* buf, const bf16x8* qf,
 __device__ __forceinline__ void finish_chunk(const u32x4* buf, f32x16 sc, int n_in_chunk, f32x16* o,
                                              SoftmaxState& st, float c2, const Lane& Lw) {
   const Lane L = opaque_lane(Lw);
-  // scores in log2 units; slots past the compacted count are masked
+  // raw scores; slots past the compacted count are masked.  The log2-unit scale c2 > 0 is
+  // applied to the maximum (rounding is monotone, so max(s) c2 = max(s c2)) and folded into
+  // one fma per score with the exponent offset below.
   if (n_in_chunk < kSlots) {
 #pragma unroll
     for (int a = 0; a < 16; ++a) {
       const int r = 8 * (a >> 2) + 4 * L.h2 + (a & 3);
-      sc[a] = r < n_in_chunk ? sc[a] * c2 : -INFINITY;
+      sc[a] = r < n_in_chunk ? sc[a] : -INFINITY;
     }
-  } else {
-#pragma unroll
-    for (int a = 0; a < 16; ++a) sc[a] *= c2;
   }
   float mx = sc[0];
 #pragma unroll
   for (int a = 1; a < 16; ++a) mx = fmaxf(mx, sc[a]);
-  mx = half_swap_max(mx);
+  mx = half_swap_max(mx) * c2;
   // lazy rescale: move the reference only when a score exceeds it by > 2^8 (exact either way)
   const bool move = mx > st.mref + kRescaleLog2;
   if (__builtin_amdgcn_ballot_w64(move) != 0) {
@@ -221,7 +220,7 @@ __device__ __forceinline__ void finish_chunk(const u32x4* buf, f32x16 sc, int n_
   float rs = 0.f;
 #pragma unroll
   for (int a = 0; a < 16; ++a) {
-    const float e = fast_exp2(sc[a] - mu);
+    const float e = fast_exp2(__builtin_fmaf(sc[a], c2, -mu));
     sc[a] = e;
     rs += e;
   }
