@@ -166,6 +166,24 @@ int32_t varlen_attn_bwd(const swa_tensor* q, const swa_tensor* k, const swa_tens
                         swa_tensor* dv, float* dsinks, float* delta, void* stream);
 
 /*
+ * varlen_attn_bwd_noalloc — varlen_attn_bwd for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation).
+ *
+ * Same arguments, semantics, kernels and results as varlen_attn_bwd, without `delta`: the
+ * per-row workspace lives in a library-owned device array of 2^22 floats (16 MiB) per device,
+ * resolved once per device and held until the process ends; the call allocates nothing.
+ * Limit: T * Hq <= 4,194,304 (SWA_ERR_UNSUPPORTED beyond, nothing enqueued). Every call on a
+ * device shares that device's array, so calls that overlap on one device (different streams,
+ * or concurrent host threads without ordering) race and must not be issued; calls ordered on
+ * one stream are safe. The array is the current device's: `stream` must belong to it.
+ */
+int32_t varlen_attn_bwd_noalloc(const swa_tensor* q, const swa_tensor* k, const swa_tensor* v,
+                                const swa_tensor* out, const swa_tensor* dout, const float* lse,
+                                const int32_t* cu_seqlens, int32_t n_docs, int32_t window, float scale,
+                                const float* sinks, swa_tensor* dq, swa_tensor* dk, swa_tensor* dv,
+                                float* dsinks, void* stream);
+
+/*
  * sparse_mla_fwd — sparse MLA forward over gathered top-k latent rows.
  *
  * For token t, head h and slot r of indices[t,:] (idx = indices[t,r]):

@@ -25,7 +25,7 @@ _DTYPES = {torch.float32: SWA_DTYPE_F32, torch.bfloat16: SWA_DTYPE_BF16, torch.i
 
 # functions the header declares, with their ctypes signatures
 EXPORTS = ("varlen_attn_fwd", "varlen_attn_bwd", "sparse_mla_fwd", "mla_value_proj", "swa_strerror", "swa_last_error",
-           "swa_abi_version", "swa_peak_mfma_bf16", "swa_peak_mfma_bf16_flops", "swa_peak_copy", "swa_peak_read")
+           "swa_abi_version", "varlen_attn_bwd_noalloc", "swa_peak_mfma_bf16", "swa_peak_mfma_bf16_flops", "swa_peak_copy", "swa_peak_read")
 
 
 class SwaTensor(ctypes.Structure):
@@ -59,6 +59,8 @@ def load_library():
         lib.varlen_attn_fwd.restype = i32
         lib.varlen_attn_bwd.argtypes = [P, P, P, P, P, vp, vp, i32, i32, f32, vp, P, P, P, vp, vp, vp]
         lib.varlen_attn_bwd.restype = i32
+        lib.varlen_attn_bwd_noalloc.argtypes = [P, P, P, P, P, vp, vp, i32, i32, f32, vp, P, P, P, vp, vp]
+        lib.varlen_attn_bwd_noalloc.restype = i32
         lib.sparse_mla_fwd.argtypes = [P, P, P, P, vp, f32, P, vp, vp]
         lib.sparse_mla_fwd.restype = i32
         lib.mla_value_proj.argtypes = [P, P, P, vp]
@@ -233,6 +235,40 @@ def varlen_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torc
                              int(window), float(scale), _ptr(sinks), *(ctypes.byref(d) for d in ds[5:]),
                              _ptr(dsinks), _ptr(delta), _stream(stream))
     _check("varlen_attn_bwd", st)
+    return dq, dk, dv, (dsinks if sinks is not None else None)
+
+
+def varlen_attn_bwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
+                            dout: torch.Tensor, lse: torch.Tensor, cu_seqlens: Optional[torch.Tensor],
+                            n_docs: Optional[int] = None, window: int = 0, scale: Optional[float] = None,
+                            sinks: Optional[torch.Tensor] = None, dq: torch.Tensor = None, dk: torch.Tensor = None,
+                            dv: torch.Tensor = None, dsinks: Optional[torch.Tensor] = None, stream=None):
+    """varlen_attn_bwd with its workspace in the library's device array (no allocation anywhere:
+    dq, dk, dv and, with sinks, dsinks must be given).  Returns (dq, dk, dv, dsinks)."""
+    lib = load_library()
+    T, Hq, D = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if n_docs is None:
+        n_docs = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
+    if dq is None or dk is None or dv is None or (sinks is not None and dsinks is None):
+        raise ValueError("varlen_attn_bwd_noalloc allocates nothing: pass dq, dk, dv (and dsinks with sinks)")
+    dev = _operand_device(q)
+    for name, x in (("k", k), ("v", v), ("out", out), ("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv)):
+        _on_gpu(name, x, dev)
+    _on_gpu("lse", lse, dev, torch.float32, contiguous=True, shape=(T, Hq))
+    if int(n_docs) > 0:
+        if cu_seqlens is None:
+            raise ValueError("cu_seqlens is required when n_docs > 0")
+        _on_gpu("cu_seqlens", cu_seqlens, dev, torch.int32, contiguous=True, min_numel=int(n_docs) + 1)
+    if sinks is not None:
+        _on_gpu("sinks", sinks, dev, torch.float32, contiguous=True, shape=(Hq,))
+        _on_gpu("dsinks", dsinks, dev, torch.float32, contiguous=True, shape=(Hq,))
+    ds = [describe(x) for x in (q, k, v, out, dout, dq, dk, dv)]
+    st = lib.varlen_attn_bwd_noalloc(*(ctypes.byref(d) for d in ds[:5]), _ptr(lse), _ptr(cu_seqlens), int(n_docs),
+                                     int(window), float(scale), _ptr(sinks), *(ctypes.byref(d) for d in ds[5:]),
+                                     _ptr(dsinks), _stream(stream))
+    _check("varlen_attn_bwd_noalloc", st)
     return dq, dk, dv, (dsinks if sinks is not None else None)
 
 

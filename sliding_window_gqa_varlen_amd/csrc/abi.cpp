@@ -63,6 +63,12 @@ bool same_data(const swa_tensor* a, const swa_tensor* b) { return a->data != nul
 
 }  // namespace
 
+namespace swa {
+// Sets the calling thread's swa_last_error() detail and returns `code` (for entry points
+// defined outside this file).
+int32_t abi_fail(int32_t code, const char* detail) { return fail(code, "%s", detail); }
+}  // namespace swa
+
 extern "C" {
 
 int32_t swa_abi_version(void) { return SWA_ABI_VERSION; }
