@@ -336,7 +336,12 @@ __device__ __forceinline__ void pv_tile(const u32x4* vbuf, const f32x16 (&sc)[2]
 }
 
 // One pipelined step in program order: S(j) = K(j) Q^T on the MFMA unit while the
-// exponentials of tile j-1 run on the VALU, then O += V(j-1) P(j-1).  Operand fragments
+// exponentials of tile j-1 run on the VALU, then O += V(j-1) P(j-1).  For head_dim 128 the
+// last 8 exponentials of a lane (the B operand of the last PV k-step) run in the PV slots
+// before that k-step instead, which evens out the VALU work between the two halves of the
+// step (a wave64 VALU op issues in 4 cycles, an exponential in 8, and a 32x32x16 MFMA keeps
+// the VALU from issuing for about half of its 32 cycles; measured 1-1.5 % faster, while head_dim
+// 256 ran 3 % slower and keeps the plain order).  Operand fragments
 // stream from LDS kAhead MFMAs ahead of their use (K fragments first, then the transposed
 // V fragments), so each MFMA waits only for a read issued long before.  Every slot is
 // fenced with sched_barrier: the emitted order is exactly this one.
@@ -348,9 +353,9 @@ __device__ __forceinline__ float qk_pv_step(const u32x4* kbuf, const u32x4* vbuf
   using B = Bf<D>;
   constexpr int NQ = 2 * B::kQFrags;  // QK^T MFMAs (32 for D = 256, 16 for D = 128, 8 for D = 64)
   constexpr int NP = 4 * B::kDBlocks; // PV MFMAs
-  constexpr int EPM = 32 / NQ;        // exponentials per QK^T MFMA slot
+  constexpr int KS = D == 128 ? 24 : 32;  // exponentials in the QK^T slots; the rest run in PV slots
+  constexpr int NP3 = 3 * NP / 4;          // PV slots before the last k-step
   constexpr int kAhead = (D >= 128) ? kAhead128 : kAhead64;
-  static_assert(32 % NQ == 0, "the 32 exponentials split evenly over the QK^T slots");
   u32x4 frag[NQ + NP];
   __builtin_amdgcn_s_setprio(1);  // the wave in its MFMA stream goes first
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): nothing older is in flight, later waits count exactly
@@ -372,24 +377,25 @@ __device__ __forceinline__ float qk_pv_step(const u32x4* kbuf, const u32x4* vbuf
   bf16x8 pb[4];
   f32x8 pf;
   float rs = 0.f;
+  // exponential x of tile j-1 (block x / 16, accumulator x % 16); every 8 form a B operand
+  auto exp_step = [&](int x) {
+    pf[x & 7] = fast_exp2(__builtin_fmaf(sc[x >> 4][x & 15], c2, -mu));
+    asm volatile("" : "+v"(pf[x & 7]));  // this slot's exponentials stay in this slot
+    if ((x & 7) == 7) {
+      pb[x >> 3] = cvt_bf16x8(pf);
+#pragma unroll
+      for (int h = 0; h < 8; ++h) rs += pf[h];
+    }
+  };
 #pragma unroll
   for (int i = 0; i < NQ; ++i) {
     sn[i & 1] = mfma_bf16_32x32x16(__builtin_bit_cast(bf16x8, frag[i]), qf[i >> 1], sn[i & 1]);
     if (i + kAhead < NQ + NP) read(i + kAhead);
 #pragma unroll
-    for (int e = 0; e < EPM; ++e) {
-      const int x = i * EPM + e;  // element of tile j-1: block x / 16, accumulator x % 16
-      pf[x & 7] = fast_exp2(__builtin_fmaf(sc[x >> 4][x & 15], c2, -mu));
-      asm volatile("" : "+v"(pf[x & 7]));  // this slot's exponentials stay in this slot
-      if ((x & 7) == 7) {
-        pb[x >> 3] = cvt_bf16x8(pf);
-#pragma unroll
-        for (int h = 0; h < 8; ++h) rs += pf[h];
-      }
-    }
+    for (int x = KS * i / NQ; x < KS * (i + 1) / NQ; ++x) exp_step(x);
     __builtin_amdgcn_sched_barrier(0);
   }
-  asm volatile("" ::"v"(rs));  // the row sum is finished inside the stream
+  if constexpr (KS == 32) asm volatile("" ::"v"(rs));  // the row sum is finished inside the stream
   // the 16 max steps (two new scores each) over the NP PV slots: steps [16 i / NP, 16 (i + 1) / NP)
   float mx = -INFINITY;
 #pragma unroll
@@ -397,6 +403,12 @@ __device__ __forceinline__ float qk_pv_step(const u32x4* kbuf, const u32x4* vbuf
     const int ks = i / B::kDBlocks, d = i % B::kDBlocks;
     o[d] = mfma_bf16_32x32x16(__builtin_bit_cast(bf16x8, frag[NQ + i]), pb[ks], o[d]);
     if (NQ + i + kAhead < NQ + NP) read(NQ + i + kAhead);
+    if constexpr (KS < 32) {
+      if (i < NP3) {
+#pragma unroll
+        for (int x = KS + (32 - KS) * i / NP3; x < KS + (32 - KS) * (i + 1) / NP3; ++x) exp_step(x);
+      }
+    }
 #pragma unroll
     for (int e = 16 * i / NP; e < 16 * (i + 1) / NP; ++e) {
       const int x = 2 * e;
@@ -406,6 +418,7 @@ __device__ __forceinline__ float qk_pv_step(const u32x4* kbuf, const u32x4* vbuf
     asm volatile("" : "+v"(mx));  // keeps this slot's share of the maximum in this slot
     __builtin_amdgcn_sched_barrier(0);
   }
+  if constexpr (KS < 32) asm volatile("" ::"v"(rs));
   sn_max = mx;
   __builtin_amdgcn_s_setprio(0);
   return rs;
