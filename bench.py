@@ -7,9 +7,10 @@ bf16, 8192 tokens in documents of 128..2048 tokens, 32 query / 8 KV heads, head_
 
 Default run: measured peaks (a bf16 MFMA-only loop, a streaming copy and read), then the
 sliding-window (1024), learned-sink window-128 and sparse MLA workloads, then the headline,
-each with W untimed warm-up steps and exactly K timed steps, back to back on the GPU; then
-the fp64 oracle on the host for each (time-capped).  One JSON line: the headline's fields at
-the top level, the other workloads under "configs", the probes under "measured_peaks".
+each with 50 ms of untimed clock-ramp steps, W untimed warm-up steps and exactly K timed
+steps, back to back on the GPU; then the fp64 oracle on the host for each (time-capped).
+One JSON line: the headline's fields at the top level, the other workloads under "configs",
+the probes under "measured_peaks".
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--no-cpu-baseline] [--copy-calibration MiB]
@@ -209,6 +210,10 @@ def cpu_baseline_vproj(inp, budget_s: float = 15.0) -> dict:
 
 
 SUITE = ("swa1024_gqa_bf16_t32768", "swa128_sink_gqa_bf16_t65536", "sparse_mla_bf16_t16384")
+# Untimed load before each case's warm-up steps: after idle the GPU's clocks take several
+# milliseconds of load to rise (window 1024 measured 598 us per step after 5 warm-up steps of
+# 2.5 ms, 512 us in steady state), so W steps alone may time the ramp.
+CLOCK_RAMP_MS = 50.0
 HEADLINE = "causal_gqa_bf16_t8192"
 
 
@@ -292,9 +297,16 @@ class Case:
         self.ms = None
 
     def timed(self, warmup: int, steps: int) -> float:
-        """W untimed steps, then exactly K steps between HIP events on the launch stream; ms per step."""
+        """Untimed steps for CLOCK_RAMP_MS of wall time (the GPU's clocks rise over several
+        milliseconds of load after idle), then W untimed steps, then exactly K steps between
+        HIP events on the launch stream; ms per step."""
         import torch
         torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        while (time.perf_counter() - t0) * 1e3 < CLOCK_RAMP_MS:
+            for _ in range(4):
+                self.step()
+            torch.cuda.synchronize()
         for _ in range(warmup):
             self.step()
         torch.cuda.synchronize()
@@ -475,14 +487,16 @@ def main() -> int:
         "config": r["config"], "roofline": r["roofline"], "cpu_baseline": None,
     }
     line["launch_us"] = spread
+    line["clock_ramp_ms"] = CLOCK_RAMP_MS
     if cold is not None:
         line["cold"] = {"us": cold, "value": head.work / (cold * 1e-6) / 1e9, "unit": r["unit"],
                         "note": "median of 5 launches, each after a 512 MiB device write that evicts the key table"}
     if suite:
         line["configs"] = {c.wl.name: c.result(peaks) for c in others}
         line["measured_peaks"] = peaks
-        line["order"] = ("probes, then " + ", ".join(SUITE) + ", then the headline, each W warm-up + K timed "
-                         "steps back to back on the GPU; oracle baselines on the host afterwards")
+        line["order"] = ("probes, then " + ", ".join(SUITE) + ", then the headline, each 50 ms of clock-ramp "
+                         "steps + W warm-up + K timed steps back to back on the GPU; oracle baselines on the host "
+                         "afterwards")
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = head.cpu_baseline(10.0)
         for c in others:
