@@ -230,11 +230,18 @@ __device__ __forceinline__ void finish_chunk(const u32x4* buf, f32x16 sc, int n_
   // only in bit 3, which flips bit 1 of lat_key
   const int r0 = 4 * L.h2 + (L.j16 >> 2);
   const int xsub = (L.j16 & 3) >> 1;
-  const int half_el = (L.j16 & 1) * 4;      // element offset inside the 16-byte unit
   const int key0 = lat_key(r0);
-  int lowp[4];
+  // byte offsets of this lane's two reads for output blocks d with d & 3 = e at k-step 0 (rows r0
+  // and r0 + 8; unit (4 e + 2 dh + xsub) ^ key0, and that unit ^ 2 for row r0 + 8); k-step s and
+  // d >> 2 add the compile-time constant (16 s kLatUnits + 16 (d >> 2)) * 16
+  const int row_b = (r0 * kLatUnits + 32 * L.half) * 16 + (L.j16 & 1) * 8;
+  int lo_b[4], hi_b[4];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) lowp[e] = (4 * e + 2 * L.dh + xsub) ^ key0;
+  for (int e = 0; e < 4; ++e) {
+    const int u = (4 * e + 2 * L.dh + xsub) ^ key0;
+    lo_b[e] = row_b + u * 16;
+    hi_b[e] = row_b + 8 * kLatUnits * 16 + (u ^ 2) * 16;
+  }
   bf16x8 pb[2];
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
@@ -244,18 +251,15 @@ __device__ __forceinline__ void finish_chunk(const u32x4* buf, f32x16 sc, int n_
     pb[s] = cvt_bf16x8(pf);
   }
   // 16 MFMAs (k-step s = i / 8, output block d = i % 8), fragments read kPvAhead ahead
-  const __bf16* elems = (const __bf16*)buf;
+  const char* bytes = (const char*)buf;
   bf16x8 vf[2 * kDBlocks];
   auto read = [&](int i) {
     const int s = i / kDBlocks, d = i % kDBlocks;
-    const int off0 = ((r0 + 16 * s) * kLatUnits + 32 * L.half) * 8 + half_el;
-    const int unit = 16 * (d >> 2) + lowp[d & 3];
+    const int c = (16 * s * kLatUnits + 16 * (d >> 2)) * 16;
     // one integer index per read keeps the pointer a single GEP from the LDS buffer, so the
     // read keeps the buffer's alias scope (no wait on gathers into the other buffers)
-    const int i_lo = off0 + unit * 8;
-    const int i_hi = off0 + 8 * kLatUnits * 8 + (unit ^ 2) * 8;
-    const bf16x4 lo4 = lds_read_tr4(&elems[i_lo]);
-    const bf16x4 hi4 = lds_read_tr4(&elems[i_hi]);
+    const bf16x4 lo4 = lds_read_tr4((const __bf16*)&bytes[lo_b[d & 3] + c]);
+    const bf16x4 hi4 = lds_read_tr4((const __bf16*)&bytes[hi_b[d & 3] + c]);
     vf[i] = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
   };
   __builtin_amdgcn_s_setprio(1);
@@ -368,7 +372,9 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_fwd_kernel(SparseMlaPa
     auto phase = [&](int cc, const u32x4* cur, u32x4* ahead, bool steady) {
       if (steady) wait_vmcnt<kDmaPerWave>(); else wait_vmcnt<0>();
       barrier_keep_loads();  // chunk cc landed for every wave; chunk cc - 1 fully consumed
-      f32x16 sc = group_ok ? qk_partial<DR>(cur, qf, L) : f32x16{};
+      // every wave computes its partial scores: the waves of a head group past H hold the
+      // clamped head's Q rows and their scores are never read (no zero vector per chunk)
+      f32x16 sc = qk_partial<DR>(cur, qf, L);
       const int xl = opaque_lane(L).lane;  // rederived, not kept live across the loop
       f32x4* mine = exch + L.wave * (4 * 64) + xl;
 #pragma unroll
