@@ -232,3 +232,66 @@ def test_nope_full_size_sampled(gpu):
     ref_o, ref_l = sparse_mla_ref_rows(inp["q"], inp["latent"], inp["k_pe"], inp["indices"], inp["doc_ids"],
                                        inp["scale"], toks)
     check(out[toks], lse[toks], ref_o, ref_l)
+
+
+def torch_sparse_rows(q, lat, kpe, idx, ids, scale, t0, t1):
+    """A plain fp32 restatement of the sparse MLA definition on the GPU (torch ops only) for
+    tokens t0 .. t1 - 1: slot k of token t is valid iff 0 <= idx < T, idx <= t and both tokens
+    lie in the same document (doc id >= 0); scores scale * q . [latent, k_pe] over the valid
+    slots; out = softmax-weighted latent rows, lse = log of the denominator; empty rows give
+    zeros and -inf."""
+    T = q.shape[0]
+    ii = idx[t0:t1].long()
+    tt = torch.arange(t0, t1, device=q.device)[:, None]
+    ic = ii.clamp(0, T - 1)
+    valid = (ii >= 0) & (ii < T) & (ii <= tt) & (ids[ic] == ids[t0:t1, None]) & (ids[t0:t1, None] >= 0)
+    keys = torch.cat([lat, kpe], dim=1)[ic]                                  # [C, K, 512 + d_rope]
+    s = torch.bmm(q[t0:t1], keys.transpose(1, 2).contiguous()) * scale        # [C, H, K]
+    s = s.masked_fill(~valid[:, None, :], float("-inf"))
+    lse = torch.logsumexp(s, dim=-1)                                          # -inf for empty rows
+    p = torch.exp(s - lse[..., None]).nan_to_num(0.0)
+    out = torch.bmm(p, lat[ic].contiguous())                                  # [C, H, 512]
+    return out, lse
+
+
+def full_rows_against_torch(inp, chunk=256, n_pin=48, seed=5):
+    """Every row of the full-size kernel output against torch_sparse_rows; that reference is first
+    pinned to the fp64 oracle on sampled tokens."""
+    f = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to("cuda:0").float()
+    q, lat, kpe = f(inp["q"]), f(inp["latent"]), f(inp["k_pe"])
+    idx = torch.from_numpy(np.ascontiguousarray(inp["indices"])).to("cuda:0")
+    ids = torch.from_numpy(np.ascontiguousarray(inp["doc_ids"])).to("cuda:0")
+    T = q.shape[0]
+    rng = np.random.default_rng(seed)
+    pin = np.unique(rng.integers(0, T, n_pin))
+    ref_o, ref_l = sparse_mla_ref_rows(inp["q"], inp["latent"], inp["k_pe"], inp["indices"], inp["doc_ids"],
+                                       inp["scale"], pin)
+    for j, t in enumerate(pin):
+        o_t, l_t = torch_sparse_rows(q, lat, kpe, idx, ids, inp["scale"], int(t), int(t) + 1)
+        np.testing.assert_allclose(o_t[0].cpu().numpy(), ref_o[j], rtol=0, atol=1e-4)
+        assert_lse_match(l_t[0].cpu().numpy().astype(np.float64), ref_l[j], 1e-4, "torch reference lse")
+    out, lse = run_sparse(inp)
+    worst_o, worst_l = 0.0, 0.0
+    for t0 in range(0, T, chunk):
+        t1 = min(T, t0 + chunk)
+        o_ref, l_ref = torch_sparse_rows(q, lat, kpe, idx, ids, inp["scale"], t0, t1)
+        o_ref, l_ref = o_ref.cpu().numpy(), l_ref.cpu().numpy().astype(np.float64)
+        worst_o = max(worst_o, float(np.abs(out[t0:t1] - o_ref).max()))
+        assert_lse_match(lse[t0:t1], l_ref, BF16_MAX_ABS)
+        fin = np.isfinite(l_ref)
+        if fin.any():
+            worst_l = max(worst_l, float(np.abs(lse[t0:t1][fin] - l_ref[fin]).max()))
+    assert worst_o <= BF16_MAX_ABS, f"out max abs error {worst_o:.3e} over all rows"
+    return worst_o, worst_l
+
+
+def test_full_size_every_row_against_a_pinned_gpu_fp32_reference(gpu):
+    """All 16384 x 128 rows of the full-size workload (the oracle finishes only sampled rows at
+    this size)."""
+    full_rows_against_torch(W.make_sparse(W.WORKLOADS[4]))
+
+
+def test_nope_full_size_every_row_against_a_pinned_gpu_fp32_reference(gpu):
+    import dataclasses
+    w = dataclasses.replace(W.WORKLOADS[4], name="sparse_mla_nope", d_rope=0, scale=1.0 / math.sqrt(512.0))
+    full_rows_against_torch(W.make_sparse(w))

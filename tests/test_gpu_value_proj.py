@@ -85,6 +85,21 @@ def test_projection_full_size_sampled(gpu):
     check_proj(got[toks], mla_value_proj_ref(o[toks], w))
 
 
+def test_projection_full_size_every_element_against_a_pinned_gpu_fp32_reference(gpu):
+    """Every element of the bench shape against a plain fp32 torch restatement on the GPU
+    (per head [T, 512] x [512, Dv]), which is first pinned to the fp64 oracle on sampled tokens."""
+    T, H, Dv = 16384, 128, 128
+    o = o_latent(25, T, H)
+    w = W.make_value_weight(26, H, Dv)
+    got = run_proj(dev(o, torch.bfloat16), dev(w, torch.bfloat16))
+    of = torch.from_numpy(o).to("cuda:0").float().permute(1, 0, 2).contiguous()       # [H, T, 512]
+    wt = torch.from_numpy(w).to("cuda:0").float().transpose(1, 2).contiguous()        # [H, 512, Dv]
+    ref = torch.bmm(of, wt).permute(1, 0, 2).contiguous().cpu().numpy().astype(np.float64)  # [T, H, Dv]
+    toks = np.unique(np.random.default_rng(9).integers(0, T, 64))
+    np.testing.assert_allclose(ref[toks], mla_value_proj_ref(o[toks], w), rtol=0, atol=1e-4)
+    check_proj(got, ref)
+
+
 def test_projection_repeat_runs_are_bitwise_identical(gpu):
     o = dev(o_latent(27, 600, 16), torch.bfloat16)
     w = dev(W.make_value_weight(28, 16, 128), torch.bfloat16)
