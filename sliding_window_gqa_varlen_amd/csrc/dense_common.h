@@ -145,6 +145,18 @@ __device__ __forceinline__ Cols make_cols(const DenseFwdParams& p, const Tile& w
   return c;
 }
 
+// The lane-dependent fields of `c` recomputed from an opaque lane id.  Code after the key loop
+// uses this copy, so the loop does not hold those values in registers for it.
+__device__ __forceinline__ Cols fresh_lane_cols(const Cols& c, int hb_shift, const Tile& w) {
+  Cols r = c;
+  r.lane = opaque((int)threadIdx.x & 63);
+  r.n = r.lane & 31;
+  r.h2 = r.lane >> 5;
+  r.tq = c.tw0 + (r.n >> hb_shift);
+  r.hq = w.h0 + (r.n & (w.HB - 1));
+  return r;
+}
+
 // Does the wave see any key of the tile starting at kb?  Does the tile need masking?
 __device__ __forceinline__ bool tile_active(const Cols& c, int kb) {
   return (c.tw0 <= c.tw1) && (kb <= c.tw1) && (c.W == 0 || kb + kBN - 1 > c.tw0 - c.W);
@@ -204,13 +216,21 @@ __device__ __forceinline__ void store_out_bf16(void* out, int64_t st, int64_t sh
       *(bf16x4*)(img + c.n * (2 * D) + (((4 * d + i) ^ out_key<D>(c.n)) << 4) + 8 * c.h2) = cvt_bf16x4(r);
     }
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's own writes, in order
+  // Store k writes column n = k kCols + n0 (n0 = lane / U < kCols).  The bits of n0 and of
+  // k kCols do not overlap, so the token (n >> hb_shift) and head (n & (HB - 1)) offsets of n
+  // are sums of a lane part (from n0) and a uniform part (from k): the 64-bit address is
+  // formed once per lane, and each store adds a uniform offset.
   const int u = c.lane % U;
+  const int n0 = opaque(c.lane / U);  // the columns n are not shared with the loop's addresses
+  const int t_lane = n0 >> hb_shift;
+  __bf16* base = (__bf16*)out + (int64_t)(c.tw0 + t_lane) * st + (int64_t)(w.h0 + (n0 & (w.HB - 1))) * sh + 8 * u;
+  const int t_last = c.tw1 - c.tw0 - t_lane;  // uniform token offsets beyond it are past the end
 #pragma unroll
   for (int k = 0; k < 32 / kCols; ++k) {
-    const int n = k * kCols + c.lane / U;
+    const int n = k * kCols + n0;
     const u32x4 val = *(const u32x4*)(img + n * (2 * D) + ((u ^ out_key<D>(n)) << 4));
-    const int t = c.tw0 + (n >> hb_shift);
-    if (t <= c.tw1) *(u32x4*)((__bf16*)out + (int64_t)t * st + (int64_t)(w.h0 + (n & (w.HB - 1))) * sh + 8 * u) = val;
+    const int tk = (k * kCols) >> hb_shift, hk = (k * kCols) & (w.HB - 1);
+    if (tk <= t_last) *(u32x4*)(base + (int64_t)tk * st + (int64_t)hk * sh) = val;
   }
 }
 

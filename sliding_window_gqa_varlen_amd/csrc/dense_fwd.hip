@@ -102,11 +102,55 @@ __device__ __forceinline__ float lane_max(const f32x16 (&sc)[2]) {
   return mx;
 }
 
+__device__ __forceinline__ float block_max(const f32x16& b) {
+  float mx = -INFINITY;
+#pragma unroll
+  for (int a = 0; a < 16; ++a) mx = fmaxf(mx, b[a]);
+  return mx;
+}
+
+// Masks a diagonal / window-edge tile block by block and returns the lane maximum of what is
+// left (head_dim 256, whose one wave per SIMD has no other wave to hide the masking behind).
+// A block that needs no mask keeps its maximum (m[blk] when HaveMax, else computed); a block
+// that no query of the wave sees (all keys after the wave's last token, or all before its
+// first token's window) is set to -inf without per-score tests; only a block that the cut
+// crosses is masked score by score and its maximum taken again.
+template <bool HaveMax>
+__device__ __forceinline__ float mask_tile_max(f32x16 (&sc)[2], int kb, const Cols& c, const float (&m)[2]) {
+  const int tq4 = opaque(c.tq - 4 * c.h2);  // as in mask_tile
+  const int lo = c.W ? tq4 - c.W + 1 - kb : -(1 << 30);
+  const unsigned range = (unsigned)(tq4 - kb - lo);
+  float mx[2];
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk) {
+    const int b0 = kb + 32 * blk;
+    if (!(b0 + 31 > c.tw0 || (c.W != 0 && b0 <= c.tw1 - c.W))) {
+      mx[blk] = HaveMax ? m[blk] : block_max(sc[blk]);
+      continue;
+    }
+    if (b0 > c.tw1 || (c.W != 0 && b0 + 31 <= c.tw0 - c.W)) {
+#pragma unroll
+      for (int a = 0; a < 16; ++a) sc[blk][a] = -INFINITY;
+      mx[blk] = -INFINITY;
+      continue;
+    }
+#pragma unroll
+    for (int a = 0; a < 16; ++a) {
+      const int off = 32 * blk + 8 * (a >> 2) + (a & 3);
+      sc[blk][a] = (unsigned)(off - lo) <= range ? sc[blk][a] : -INFINITY;
+    }
+    mx[blk] = block_max(sc[blk]);
+  }
+  return fmaxf(mx[0], mx[1]);
+}
+
 // Scores -> unnormalised probabilities exp2(s * c2 - mu), in place; returns their sum.
+// NB = 1: the first 32-key block only (the second is known to be fully masked)
+template <int NB = 2>
 __device__ __forceinline__ float tile_exp(f32x16 (&sc)[2], float c2, float mu) {
   float rs = 0.f;
 #pragma unroll
-  for (int blk = 0; blk < 2; ++blk)
+  for (int blk = 0; blk < NB; ++blk)
 #pragma unroll
     for (int a = 0; a < 16; ++a) {
       const float e = fast_exp2(__builtin_fmaf(sc[blk][a], c2, -mu));
@@ -134,7 +178,9 @@ __device__ __forceinline__ void softmax_tile(f32x16 (&sc)[2], bool need_mask, in
 }
 
 // Half-wave sums combined, sink folded in; stores the LSE and returns the normaliser.
-// `st.l` holds this half-wave's share of the row sum.
+// `st.l` holds this half-wave's share of the row sum.  The normaliser comes from v_rcp_f32
+// (within 1 ulp) rather than a correctly rounded division sequence: its error is far below the
+// output's rounding.
 __device__ __forceinline__ float epilogue_scalars(const DenseFwdParams& p, const Tile& w, const Cols& c,
                                                   const Softmax& st) {
   const float lt = half_swap_sum(st.l);
@@ -145,10 +191,10 @@ __device__ __forceinline__ float epilogue_scalars(const DenseFwdParams& p, const
     const float mm = fmaxf(m2, s2);
     const float corr = fast_exp2(m2 - mm);
     const float lf = lt * corr + fast_exp2(s2 - mm);
-    inv = corr / lf;
+    inv = corr * __builtin_amdgcn_rcpf(lf);
     lse_v = (mm + __builtin_amdgcn_logf(lf)) * kLn2;
   } else {
-    inv = 1.f / lt;
+    inv = __builtin_amdgcn_rcpf(lt);
     lse_v = (m2 + __builtin_amdgcn_logf(lt)) * kLn2;
   }
   if (p.lse != nullptr && c.h2 == 0 && c.tq < w.t_end) p.lse[(int64_t)c.tq * p.Hq + c.hq] = lse_v;
@@ -320,12 +366,13 @@ __device__ __forceinline__ bf16x8 v_frag(const u32x4* vbuf, const VOffsets<D>& v
 }
 
 // O^T += V^T P^T for the tile in `vbuf` (probabilities in sc).
-template <int D>
+// NKS = 2: k-steps 0 and 1 only (keys 0-31; the second block's probabilities are zero)
+template <int D, int NKS = 4>
 __device__ __forceinline__ void pv_tile(const u32x4* vbuf, const f32x16 (&sc)[2], const VOffsets<D>& vo,
                                         f32x16 (&o)[Bf<D>::kDBlocks]) {
   using B = Bf<D>;
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
+  for (int ks = 0; ks < NKS; ++ks) {
     f32x8 pf;
 #pragma unroll
     for (int e = 0; e < 8; ++e) pf[e] = sc[ks >> 1][8 * (ks & 1) + e];
@@ -349,7 +396,7 @@ template <int D>
 __device__ __forceinline__ float qk_pv_step(const u32x4* kbuf, const u32x4* vbuf, const bf16x8 (&qf)[Bf<D>::kQFrags],
                                             int kaddr, const VOffsets<D>& vo, f32x16 (&sn)[2],
                                             const f32x16 (&sc)[2], float c2, float mu, f32x16 (&o)[Bf<D>::kDBlocks],
-                                            float& sn_max) {
+                                            float (&sn_max)[2]) {
   using B = Bf<D>;
   constexpr int NQ = 2 * B::kQFrags;  // QK^T MFMAs (32 for D = 256, 16 for D = 128, 8 for D = 64)
   constexpr int NP = 4 * B::kDBlocks; // PV MFMAs
@@ -396,8 +443,11 @@ __device__ __forceinline__ float qk_pv_step(const u32x4* kbuf, const u32x4* vbuf
     __builtin_amdgcn_sched_barrier(0);
   }
   if constexpr (KS == 32) asm volatile("" ::"v"(rs));  // the row sum is finished inside the stream
-  // the 16 max steps (two new scores each) over the NP PV slots: steps [16 i / NP, 16 (i + 1) / NP)
-  float mx = -INFINITY;
+  // the 16 max steps (two new scores each) over the NP PV slots: steps [16 i / NP, 16 (i + 1) / NP).
+  // head_dim 256 keeps one maximum per 32-key block (a masked tile takes again only a masked
+  // block's); the others one maximum in sn_max[0]
+  constexpr int NC = D == 256 ? 2 : 1;
+  float mx[2] = {-INFINITY, -INFINITY};
 #pragma unroll
   for (int i = 0; i < NP; ++i) {
     const int ks = i / B::kDBlocks, d = i % B::kDBlocks;
@@ -412,14 +462,17 @@ __device__ __forceinline__ float qk_pv_step(const u32x4* kbuf, const u32x4* vbuf
 #pragma unroll
     for (int e = 16 * i / NP; e < 16 * (i + 1) / NP; ++e) {
       const int x = 2 * e;
-      mx = fmaxf(mx, sn[x >> 4][x & 15]);
-      mx = fmaxf(mx, sn[x >> 4][(x & 15) + 1]);
+      const int ch = NC == 2 ? x >> 4 : 0;
+      mx[ch] = fmaxf(mx[ch], sn[x >> 4][x & 15]);
+      mx[ch] = fmaxf(mx[ch], sn[x >> 4][(x & 15) + 1]);
     }
-    asm volatile("" : "+v"(mx));  // keeps this slot's share of the maximum in this slot
+    asm volatile("" : "+v"(mx[0]));  // keeps this slot's share of the maximum in this slot
+    if constexpr (NC == 2) asm volatile("" : "+v"(mx[1]));
     __builtin_amdgcn_sched_barrier(0);
   }
   if constexpr (KS < 32) asm volatile("" ::"v"(rs));
-  sn_max = mx;
+  sn_max[0] = mx[0];
+  sn_max[1] = mx[1];
   __builtin_amdgcn_s_setprio(0);
   return rs;
 }
@@ -476,8 +529,15 @@ __global__ __launch_bounds__(kThreads, D == 64 ? kOcc64 : D == 128 ? 2 : 1) void
   barrier_keep_loads();
   f32x16 sc[2];
   qk_tile<D>(k0, qf, c.n, c.h2, sc);
-  if (tile_needs_mask(c, c.k_lo)) mask_tile(sc, c.k_lo, c);
-  TileStats ts = tile_stats(lane_max(sc), c2, st);
+  float s0_max;
+  if constexpr (D == 256) {
+    const float no_max[2] = {-INFINITY, -INFINITY};
+    s0_max = tile_needs_mask(c, c.k_lo) ? mask_tile_max<false>(sc, c.k_lo, c, no_max) : lane_max(sc);
+  } else {
+    if (tile_needs_mask(c, c.k_lo)) mask_tile(sc, c.k_lo, c);
+    s0_max = lane_max(sc);
+  }
+  TileStats ts = tile_stats(s0_max, c2, st);
 
   // iteration j: S(j) from K(j) ; softmax + PV of tile j-1 ; K(j+1), V(j) in flight.
   // On entry sc holds the masked scores of tile j-1 and ts their statistics.  After the
@@ -493,11 +553,18 @@ __global__ __launch_bounds__(kThreads, D == 64 ? kOcc64 : D == 128 ? 2 : 1) void
     dma_tile<D, true>(vbase, p.v_st, kb, c.k_hi, vcur_dst, c.wave, c.lane, vdl);
     rescale_o<B::kDBlocks>(ts.move, ts.alpha, o);
     f32x16 sn[2];
+    float bm[2];
+    const float rs = qk_pv_step<D>(kcur, vprev, qf, kaddr, vo, sn, sc, c2, ts.mu, o, bm);
+    // diagonal / window-edge tile: mask, then take the maximum again
     float sn_max;
-    const float rs = qk_pv_step<D>(kcur, vprev, qf, kaddr, vo, sn, sc, c2, ts.mu, o, sn_max);
-    if (tile_needs_mask(c, kb)) {  // diagonal / window-edge tile: mask, then take the max again
-      mask_tile(sn, kb, c);
-      sn_max = lane_max(sn);
+    if constexpr (D == 256) {
+      sn_max = tile_needs_mask(c, kb) ? mask_tile_max<true>(sn, kb, c, bm) : fmaxf(bm[0], bm[1]);
+    } else {
+      sn_max = bm[0];
+      if (tile_needs_mask(c, kb)) {
+        mask_tile(sn, kb, c);
+        sn_max = lane_max(sn);
+      }
     }
     st.l = st.l * ts.alpha + rs;
     ts = tile_stats(sn_max, c2, st);
@@ -510,18 +577,30 @@ __global__ __launch_bounds__(kThreads, D == 64 ? kOcc64 : D == 128 ? 2 : 1) void
     step(j + 1, k0, k1, v0, v1);
   }
   if (j < nt) step(j, k1, k0, v1, v0);
-  // last tile: its V is in buffer (nt - 1) & 1
+  // last tile: its V is in buffer (nt - 1) & 1.  When its second 32-key block starts after this
+  // wave's last token, mask_tile set all of that block's scores to -inf: their probabilities are
+  // exactly zero, so its exponentials and PV k-steps 2 and 3 are skipped (a uniform branch that
+  // leaves the result unchanged).  Not for D = 256, whose registers the second copy of the
+  // tail would spill.
   wait_vm0();
   barrier_keep_loads();
   rescale_o<B::kDBlocks>(ts.move, ts.alpha, o);
-  st.l = st.l * ts.alpha + tile_exp(sc, c2, ts.mu);
-  if ((nt - 1) & 1) pv_tile<D>(v1, sc, vo, o);
-  else pv_tile<D>(v0, sc, vo, o);
+  const bool tail_half = D != 256 && c.k_lo + (nt - 1) * kBN + 32 > c.tw1;
+  if (tail_half) {
+    st.l = st.l * ts.alpha + tile_exp<1>(sc, c2, ts.mu);
+    if ((nt - 1) & 1) pv_tile<D, 2>(v1, sc, vo, o);
+    else pv_tile<D, 2>(v0, sc, vo, o);
+  } else {
+    st.l = st.l * ts.alpha + tile_exp(sc, c2, ts.mu);
+    if ((nt - 1) & 1) pv_tile<D>(v1, sc, vo, o);
+    else pv_tile<D>(v0, sc, vo, o);
+  }
   // every wave is past its last K read (the barrier above): the K buffers hold the output
   // images, two waves per buffer
   char* img = (char*)(c.wave < 2 ? k0 : k1) + (c.wave & 1) * (64 * D);
-  const float inv = epilogue_scalars(p, w, c, st);
-  store_out_bf16<D>(p.out, p.o_st, p.o_sh, w, c, p.hb_shift, inv, o, img);
+  const Cols ce = fresh_lane_cols(c, p.hb_shift, w);
+  const float inv = epilogue_scalars(p, w, ce, st);
+  store_out_bf16<D>(p.out, p.o_st, p.o_sh, w, ce, p.hb_shift, inv, o, img);
 }
 
 // ======================================================================================
