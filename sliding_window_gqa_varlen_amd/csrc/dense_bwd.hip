@@ -69,17 +69,41 @@ __device__ __forceinline__ int row_key(int r) {
   else return (r >> 1) & 7;
 }
 
+// The lane's byte offset inside a 64-unit block of a full 64-row tile.  Transfer i of wave w
+// covers rows (4 i + w) R + lane / U; the swizzle key depends only on the low bits of the row
+// that the wave and the lane fix (R = 64 / U rows per block), so the offset is the same for
+// every transfer and every tile, and the block's row offset goes into soffset.
+template <int D, bool RT>
+__device__ __forceinline__ uint32_t rows64_lane_off(int64_t st, int lane, int wave) {
+  constexpr int U = Bw<D>::U, R = 64 / U;
+  const int lr = lane / U, lp = lane % U;
+  const int cu = lp ^ (RT ? rt_key<D>(wave * R + lr) : row_key<D>(wave * R + lr));
+  return (uint32_t)lr * ((uint32_t)st * 2u) + (uint32_t)cu * 16u;
+}
+
 // 64 rows (r0 .. r0 + 63, clamped to r_last >= r0) of D bf16 each into buf; logical unit u of
-// row r lands at physical unit u ^ key(r).  U / 4 transfers of 64 units per wave.
+// row r lands at physical unit u ^ key(r).  U / 4 transfers of 64 units per wave.  A full tile
+// takes the lane offset from rows64_lane_off and costs no VALU; a clamped (last) tile
+// recomputes every row.
 template <int D, bool RT>
 __device__ __forceinline__ void dma_rows64(const __bf16* base, int64_t st, int r0, int r_last, u32x4* buf, int wave,
-                                           int lane_in) {
+                                           int lane_in, uint32_t lane_off) {
   constexpr int U = Bw<D>::U, R = 64 / U;  // rows per 64-unit block
-  const int lane = opaque(lane_in);
   const __amdgpu_buffer_rsrc_t rsrc =
       __builtin_amdgcn_make_buffer_rsrc((void*)(base + (int64_t)r0 * st), (short)0, -1, kBufferWord3);
   const uint32_t stb = (uint32_t)st * 2u;
   const int lim = r_last - r0;
+  if (lim >= 63) {
+#pragma unroll
+    for (int i = 0; i < U / 4; ++i) {
+      const int blk = i * 4 + wave;
+      u32x4* dst = buf + __builtin_amdgcn_readfirstlane(blk * 64);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)dst, 16, lane_off,
+                                               __builtin_amdgcn_readfirstlane((uint32_t)(blk * R) * stb), 0, 0);
+    }
+    return;
+  }
+  const int lane = opaque(lane_in);
   const int lr = lane / U, lp = lane % U;
 #pragma unroll
   for (int i = 0; i < U / 4; ++i) {
@@ -286,20 +310,22 @@ __global__ __launch_bounds__(kThreads, D == 64 ? kDqOcc64 : 2) void bwd_dq_kerne
     }
   };
 
-  dma_rows64<D, true>(kbase, f.k_st, c.k_lo, last, k0, c.wave, c.lane);
-  dma_rows64<D, false>(vbase, f.v_st, c.k_lo, last, v0, c.wave, c.lane);
+  const uint32_t koff = rows64_lane_off<D, true>(f.k_st, c.lane, c.wave);
+  const uint32_t voff = rows64_lane_off<D, false>(f.v_st, c.lane, c.wave);
+  dma_rows64<D, true>(kbase, f.k_st, c.k_lo, last, k0, c.wave, c.lane, koff);
+  dma_rows64<D, false>(vbase, f.v_st, c.k_lo, last, v0, c.wave, c.lane, voff);
   int j = 0;
   for (; j + 1 < nt; j += 2) {
     wait_vm0();
     barrier_keep_loads();  // tile j landed for every wave; tile j - 1 fully consumed
-    dma_rows64<D, true>(kbase, f.k_st, c.k_lo + (j + 1) * kBN, last, k1, c.wave, c.lane);
-    dma_rows64<D, false>(vbase, f.v_st, c.k_lo + (j + 1) * kBN, last, v1, c.wave, c.lane);
+    dma_rows64<D, true>(kbase, f.k_st, c.k_lo + (j + 1) * kBN, last, k1, c.wave, c.lane, koff);
+    dma_rows64<D, false>(vbase, f.v_st, c.k_lo + (j + 1) * kBN, last, v1, c.wave, c.lane, voff);
     tile(k0, v0, c.k_lo + j * kBN);
     wait_vm0();
     barrier_keep_loads();
     if (j + 2 < nt) {
-      dma_rows64<D, true>(kbase, f.k_st, c.k_lo + (j + 2) * kBN, last, k0, c.wave, c.lane);
-      dma_rows64<D, false>(vbase, f.v_st, c.k_lo + (j + 2) * kBN, last, v0, c.wave, c.lane);
+      dma_rows64<D, true>(kbase, f.k_st, c.k_lo + (j + 2) * kBN, last, k0, c.wave, c.lane, koff);
+      dma_rows64<D, false>(vbase, f.v_st, c.k_lo + (j + 2) * kBN, last, v0, c.wave, c.lane, voff);
     }
     tile(k1, v1, c.k_lo + (j + 1) * kBN);
   }
@@ -639,11 +665,13 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void bwd_dkdv_kernel(Den
   const TrOffsets<D> to = tr_offsets<D>(lane);
   const float c2 = f.c2;
 
+  const uint32_t qoff_l = rows64_lane_off<D, true>(f.q_st, lane, wave);
+  const uint32_t ooff_l = rows64_lane_off<D, true>(p.do_st, lane, wave);
   auto issue = [&](int it, u32x4* qb, u32x4* ob, float* lb, float* db) {
     const int h = w.g * f.G + walk_head(it);
     const int i0 = w.k0 + 64 * walk_tile(it);
-    dma_rows64<D, true>((const __bf16*)f.q + (int64_t)h * f.q_sh, f.q_st, i0, i_hi - 1, qb, wave, lane);
-    dma_rows64<D, true>((const __bf16*)p.dout + (int64_t)h * p.do_sh, p.do_st, i0, i_hi - 1, ob, wave, lane);
+    dma_rows64<D, true>((const __bf16*)f.q + (int64_t)h * f.q_sh, f.q_st, i0, i_hi - 1, qb, wave, lane, qoff_l);
+    dma_rows64<D, true>((const __bf16*)p.dout + (int64_t)h * p.do_sh, p.do_st, i0, i_hi - 1, ob, wave, lane, ooff_l);
     if (wave == 0) dma_rowvals(f.lse, f.Hq, h, i0, i_hi - 1, lb, lane);
     if (wave == 1) dma_rowvals(p.delta, f.Hq, h, i0, i_hi - 1, db, lane);
   };
@@ -721,13 +749,27 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
 }
 
 // 64 rows x 128 bf16 (rt_key swizzle) into buf by 8 waves: two 4-row blocks per wave
+__device__ __forceinline__ uint32_t rows64_w8_lane_off(int64_t st, int lane, int wave) {
+  const int lr = lane >> 4, lp = lane & 15;
+  return (uint32_t)lr * ((uint32_t)st * 2u) + (uint32_t)(lp ^ rt16_key(wave * 4 + lr)) * 16u;
+}
 __device__ __forceinline__ void dma_rows64_w8(const __bf16* base, int64_t st, int r0, int r_last, u32x4* buf,
-                                              int wave, int lane_in) {
-  const int lane = opaque(lane_in);
+                                              int wave, int lane_in, uint32_t lane_off) {
   const __amdgpu_buffer_rsrc_t rsrc =
       __builtin_amdgcn_make_buffer_rsrc((void*)(base + (int64_t)r0 * st), (short)0, -1, kBufferWord3);
   const uint32_t stb = (uint32_t)st * 2u;
   const int lim = r_last - r0;
+  if (lim >= 63) {  // full tile: the lane offset of rows64_w8_lane_off, the block's rows in soffset
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int blk = i * 8 + wave;
+      u32x4* dst = buf + __builtin_amdgcn_readfirstlane(blk * 64);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)dst, 16, lane_off,
+                                               __builtin_amdgcn_readfirstlane((uint32_t)(blk * 4) * stb), 0, 0);
+    }
+    return;
+  }
+  const int lane = opaque(lane_in);
   const int lr = lane >> 4, lp = lane & 15;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
@@ -896,11 +938,13 @@ __global__ __launch_bounds__(kT16, 1) void bwd_dkdv16_kernel(DenseBwdParams p) {
   }
   const float c2 = f.c2;
 
+  const uint32_t qoff_l = rows64_w8_lane_off(f.q_st, lane, wave);
+  const uint32_t ooff_l = rows64_w8_lane_off(p.do_st, lane, wave);
   auto issue = [&](int it, u32x4* qb, u32x4* ob, float* lb, float* db) {
     const int h = w.g * f.G + walk_head(it);
     const int i0 = w.k0 + 64 * walk_tile(it);
-    dma_rows64_w8((const __bf16*)f.q + (int64_t)h * f.q_sh, f.q_st, i0, i_hi - 1, qb, wave, lane);
-    dma_rows64_w8((const __bf16*)p.dout + (int64_t)h * p.do_sh, p.do_st, i0, i_hi - 1, ob, wave, lane);
+    dma_rows64_w8((const __bf16*)f.q + (int64_t)h * f.q_sh, f.q_st, i0, i_hi - 1, qb, wave, lane, qoff_l);
+    dma_rows64_w8((const __bf16*)p.dout + (int64_t)h * p.do_sh, p.do_st, i0, i_hi - 1, ob, wave, lane, ooff_l);
     if (wave == 0) dma_rowvals(f.lse, f.Hq, h, i0, i_hi - 1, lb, lane);
     if (wave == 1) dma_rowvals(p.delta, f.Hq, h, i0, i_hi - 1, db, lane);
   };
