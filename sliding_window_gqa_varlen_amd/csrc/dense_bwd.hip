@@ -37,6 +37,7 @@
 //  * Tiles travel HBM -> LDS by buffer_load ... lds into two statically named buffers per
 //    operand (loop unrolled by two): the next tile is in flight while this one is used.
 #include <climits>
+#include <type_traits>
 
 #include "dense_common.h"
 
@@ -282,11 +283,15 @@ __global__ __launch_bounds__(kThreads, D == 64 ? kDqOcc64 : 2) void bwd_dq_kerne
   const int nt = c.n_tiles;
   const int last = c.k_hi - 1;
 
-  auto tile = [&](const u32x4* kb_, const u32x4* vb_, int kb) {
-    if (!tile_active(c, kb)) return;  // none of this wave's tokens sees these keys
+  // NB = 1: the tile's second 32-key block starts after every token of the wave, so the mask
+  // would make its probabilities and dS exactly zero: its S, dP and dQ k-steps are skipped.
+  // head_dim 64 only (a sixth of the blocks of the window-128 workload; at head_dim 128 the
+  // second copy of the tile spilled 26 dwords for about 3 % of the causal work)
+  auto tile_blocks = [&](auto nb, const u32x4* kb_, const u32x4* vb_, int kb) __attribute__((always_inline)) {
+    constexpr int NB = decltype(nb)::value;
     f32x16 sc[2], dp[2];
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
+    for (int blk = 0; blk < NB; ++blk) {
       sc[blk] = f32x16{};
       dp[blk] = f32x16{};
 #pragma unroll
@@ -294,20 +299,25 @@ __global__ __launch_bounds__(kThreads, D == 64 ? kDqOcc64 : 2) void bwd_dq_kerne
 #pragma unroll
       for (int s = 0; s < B::QF; ++s) dp[blk] = mfma_bf16_32x32x16(row_frag<D>(vb_, vraddr, blk, s), gf[s], dp[blk]);
     }
-    if (tile_needs_mask(c, kb)) mask_tile(sc, kb, c);
+    if (tile_needs_mask(c, kb)) mask_tile<NB>(sc, kb, c);
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
+    for (int blk = 0; blk < NB; ++blk)
 #pragma unroll
       for (int a = 0; a < 16; ++a) {
         const float pr = fast_exp2(__builtin_fmaf(sc[blk][a], c2, -lse2));
         sc[blk][a] = pr * (dp[blk][a] - dl);
       }
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+    for (int ks = 0; ks < 2 * NB; ++ks) {
       const bf16x8 sb = pack_ks(sc, ks);
 #pragma unroll
       for (int d = 0; d < B::DB; ++d) acc[d] = mfma_bf16_32x32x16(tr_frag<D>(kb_, to, ks, d), sb, acc[d]);
     }
+  };
+  auto tile = [&](const u32x4* kb_, const u32x4* vb_, int kb) __attribute__((always_inline)) {
+    if (!tile_active(c, kb)) return;  // none of this wave's tokens sees these keys
+    if (D == 64 && kb + 32 > c.tw1) tile_blocks(std::integral_constant<int, D == 64 ? 1 : 2>{}, kb_, vb_, kb);
+    else tile_blocks(std::integral_constant<int, 2>{}, kb_, vb_, kb);
   };
 
   const uint32_t koff = rows64_lane_off<D, true>(f.k_st, c.lane, c.wave);

@@ -169,6 +169,7 @@ __device__ __forceinline__ bool tile_needs_mask(const Cols& c, int kb) {
 // diagonal or the window edge only).  Each 32-key block is masked only when some key of it
 // lies after the wave's first query or before its last query's window (a uniform test): in a
 // window-edge or diagonal tile the other block is usually inside every query's range.
+template <int NB = 2>  // NB = 1: block 0 only (block 1 is not computed)
 __device__ __forceinline__ void mask_tile(f32x16 (&sc)[2], int kb, const Cols& c) {
   // allowed keys of this lane's query: kb + off with lo <= off <= lo + range, where
   // off = 32 blk + 8 (a / 4) + 4 h2 + a % 4; the 4 h2 term is folded into lo so every
@@ -177,7 +178,7 @@ __device__ __forceinline__ void mask_tile(f32x16 (&sc)[2], int kb, const Cols& c
   const int lo = c.W ? tq4 - c.W + 1 - kb : -(1 << 30);
   const unsigned range = (unsigned)(tq4 - kb - lo);
 #pragma unroll
-  for (int blk = 0; blk < 2; ++blk) {
+  for (int blk = 0; blk < NB; ++blk) {
     const int b0 = kb + 32 * blk;
     if (!(b0 + 31 > c.tw0 || (c.W != 0 && b0 <= c.tw1 - c.W))) continue;
 #pragma unroll
