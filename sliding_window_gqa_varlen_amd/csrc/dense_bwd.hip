@@ -495,12 +495,27 @@ __device__ __forceinline__ bool decode_key_tile(const DenseBwdParams& p, KeyTile
 // Measured on the causal 8192-token backward: the dk/dv kernel fetched 845 MiB beyond L2 in
 // document order, 340 MiB with this walk (its Q, dO, K, V, lse and delta come to 162 MiB); on the
 // window-1024 one 2176 -> 1342 MiB (minimum 584).
+// Step `it` of the walk visits head head(it) and query tile tile(it).  The kernels advance a
+// WalkPos one step at a time (compares instead of the divisions, which cost about a hundred
+// scalar instructions per step); the two forms agree at every step.
+struct WalkPos {
+  int head, tile, s;  // s: position in the inner loop of the rotated walk
+};
 struct QueryWalk {
   bool down;  // from the document end, heads inner
   int rot;    // rotation of the sliding-window walk
   __device__ __forceinline__ int head(int it, int G, int n_qt) const { return down ? it % G : it / n_qt; }
   __device__ __forceinline__ int tile(int it, int G, int n_qt) const {
     return down ? n_qt - 1 - it / G : (it % n_qt + rot) % n_qt;
+  }
+  __device__ __forceinline__ WalkPos first(int n_qt) const {
+    return down ? WalkPos{0, n_qt - 1, 0} : WalkPos{0, rot >= n_qt ? rot - n_qt : rot, 0};
+  }
+  __device__ __forceinline__ WalkPos next(const WalkPos& p, int G, int n_qt) const {
+    if (down) return p.head + 1 == G ? WalkPos{0, p.tile - 1, 0} : WalkPos{p.head + 1, p.tile, 0};
+    const bool wrap = p.s + 1 == n_qt;
+    const int s1 = wrap ? 0 : p.s + 1;
+    return WalkPos{wrap ? p.head + 1 : p.head, s1 + rot >= n_qt ? s1 + rot - n_qt : s1 + rot, s1};
   }
 };
 __device__ __forceinline__ QueryWalk query_walk(const KeyTile& w, int i_hi, int n_qt) {
@@ -669,24 +684,22 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void bwd_dkdv_kernel(Den
   const int n_qt = (i_hi - w.k0 + 63) / 64;
   const int n_it = f.G * n_qt;
   const QueryWalk walk = query_walk(w, i_hi, n_qt);
-  auto walk_head = [&](int it) { return walk.head(it, f.G, n_qt); };
-  auto walk_tile = [&](int it) { return walk.tile(it, f.G, n_qt); };
   const int raddr = n * B::U * 16 + ((h2 ^ rt_key<D>(n)) << 4);
   const TrOffsets<D> to = tr_offsets<D>(lane);
   const float c2 = f.c2;
 
   const uint32_t qoff_l = rows64_lane_off<D, true>(f.q_st, lane, wave);
   const uint32_t ooff_l = rows64_lane_off<D, true>(p.do_st, lane, wave);
-  auto issue = [&](int it, u32x4* qb, u32x4* ob, float* lb, float* db) {
-    const int h = w.g * f.G + walk_head(it);
-    const int i0 = w.k0 + 64 * walk_tile(it);
+  auto issue = [&](const WalkPos& wp, u32x4* qb, u32x4* ob, float* lb, float* db) {
+    const int h = w.g * f.G + wp.head;
+    const int i0 = w.k0 + 64 * wp.tile;
     dma_rows64<D, true>((const __bf16*)f.q + (int64_t)h * f.q_sh, f.q_st, i0, i_hi - 1, qb, wave, lane, qoff_l);
     dma_rows64<D, true>((const __bf16*)p.dout + (int64_t)h * p.do_sh, p.do_st, i0, i_hi - 1, ob, wave, lane, ooff_l);
     if (wave == 0) dma_rowvals(f.lse, f.Hq, h, i0, i_hi - 1, lb, lane);
     if (wave == 1) dma_rowvals(p.delta, f.Hq, h, i0, i_hi - 1, db, lane);
   };
-  auto step = [&](int it, const u32x4* qb, const u32x4* ob, const float* lb, const float* db) {
-    const int i0 = w.k0 + 64 * walk_tile(it);
+  auto step = [&](const WalkPos& wp, const u32x4* qb, const u32x4* ob, const float* lb, const float* db) {
+    const int i0 = w.k0 + 64 * wp.tile;
     // wave-uniform: skip tiles none of whose queries sees this wave's keys
     if (!has_keys || i0 + 63 < kw0 || (W != 0 && i0 > kw0 + 31 + W - 1)) return;
     const bool need_mask = !(i0 >= kw0 + 31 && i0 + 63 < e_doc && (W == 0 || i0 + 63 - kw0 < W));
@@ -696,22 +709,26 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void bwd_dkdv_kernel(Den
       dkdv_tile<D, false>(qb, ob, lb, db, kf, vf, raddr, to, c2, dk, dv, i0 - key, e_doc - key, W, h2);
   };
 
-  issue(0, q0, o0, ls0, dl0);
+  WalkPos p0 = walk.first(n_qt);
+  issue(p0, q0, o0, ls0, dl0);
   int it = 0;
   for (; it + 1 < n_it; it += 2) {
+    const WalkPos p1 = walk.next(p0, f.G, n_qt);
     wait_vm0();
     barrier_keep_loads();  // tile it landed for every wave; tile it - 1 fully consumed
-    issue(it + 1, q1, o1, ls1, dl1);
-    step(it, q0, o0, ls0, dl0);
+    issue(p1, q1, o1, ls1, dl1);
+    step(p0, q0, o0, ls0, dl0);
+    const WalkPos p2 = walk.next(p1, f.G, n_qt);
     wait_vm0();
     barrier_keep_loads();
-    if (it + 2 < n_it) issue(it + 2, q0, o0, ls0, dl0);
-    step(it + 1, q1, o1, ls1, dl1);
+    if (it + 2 < n_it) issue(p2, q0, o0, ls0, dl0);
+    step(p1, q1, o1, ls1, dl1);
+    p0 = p2;
   }
   if (it < n_it) {
     wait_vm0();
     barrier_keep_loads();
-    step(it, q0, o0, ls0, dl0);
+    step(p0, q0, o0, ls0, dl0);
   }
 
   if (has_keys && key < w.k1) {
@@ -935,8 +952,6 @@ __global__ __launch_bounds__(kT16, 1) void bwd_dkdv16_kernel(DenseBwdParams p) {
   const int n_qt = (i_hi - w.k0 + 63) / 64;
   const int n_it = f.G * n_qt;
   const QueryWalk walk = query_walk(w, i_hi, n_qt);
-  auto walk_head = [&](int it) { return walk.head(it, f.G, n_qt); };
-  auto walk_tile = [&](int it) { return walk.tile(it, f.G, n_qt); };
   // row reads: row 16 b + n, logical unit 4 s + g -> physical (4 s + g) ^ key(n) = (g ^ key(n)) ^ 4 s
   const int raddr = n * U * 16 + ((g ^ rt16_key(n)) << 4);
   int toff[8];  // transposed reads: supplier row 4 g + n / 4 (+ 32 s, + 16), columns 16 m + 4 (n % 4)
@@ -950,16 +965,16 @@ __global__ __launch_bounds__(kT16, 1) void bwd_dkdv16_kernel(DenseBwdParams p) {
 
   const uint32_t qoff_l = rows64_w8_lane_off(f.q_st, lane, wave);
   const uint32_t ooff_l = rows64_w8_lane_off(p.do_st, lane, wave);
-  auto issue = [&](int it, u32x4* qb, u32x4* ob, float* lb, float* db) {
-    const int h = w.g * f.G + walk_head(it);
-    const int i0 = w.k0 + 64 * walk_tile(it);
+  auto issue = [&](const WalkPos& wp, u32x4* qb, u32x4* ob, float* lb, float* db) {
+    const int h = w.g * f.G + wp.head;
+    const int i0 = w.k0 + 64 * wp.tile;
     dma_rows64_w8((const __bf16*)f.q + (int64_t)h * f.q_sh, f.q_st, i0, i_hi - 1, qb, wave, lane, qoff_l);
     dma_rows64_w8((const __bf16*)p.dout + (int64_t)h * p.do_sh, p.do_st, i0, i_hi - 1, ob, wave, lane, ooff_l);
     if (wave == 0) dma_rowvals(f.lse, f.Hq, h, i0, i_hi - 1, lb, lane);
     if (wave == 1) dma_rowvals(p.delta, f.Hq, h, i0, i_hi - 1, db, lane);
   };
-  auto step = [&](int it, const u32x4* qb, const u32x4* ob, const float* lb, const float* db) {
-    const int i0 = w.k0 + 64 * walk_tile(it);
+  auto step = [&](const WalkPos& wp, const u32x4* qb, const u32x4* ob, const float* lb, const float* db) {
+    const int i0 = w.k0 + 64 * wp.tile;
     if (!has_keys || i0 + 63 < kw0 || (W != 0 && i0 > kw0 + 15 + W - 1)) return;
     const bool need_mask = !(i0 >= kw0 + 15 && i0 + 63 < e_doc && (W == 0 || i0 + 63 - kw0 < W));
     if (need_mask)
@@ -968,22 +983,26 @@ __global__ __launch_bounds__(kT16, 1) void bwd_dkdv16_kernel(DenseBwdParams p) {
       dkdv16_tile<false>(qb, ob, lb, db, kf, vf, raddr, toff, c2, dk, dv, i0 - key, e_doc - key, W, g);
   };
 
-  issue(0, q0, o0, ls0, dl0);
+  WalkPos p0 = walk.first(n_qt);
+  issue(p0, q0, o0, ls0, dl0);
   int it = 0;
   for (; it + 1 < n_it; it += 2) {
+    const WalkPos p1 = walk.next(p0, f.G, n_qt);
     wait_vm0();
     barrier_keep_loads();
-    issue(it + 1, q1, o1, ls1, dl1);
-    step(it, q0, o0, ls0, dl0);
+    issue(p1, q1, o1, ls1, dl1);
+    step(p0, q0, o0, ls0, dl0);
+    const WalkPos p2 = walk.next(p1, f.G, n_qt);
     wait_vm0();
     barrier_keep_loads();
-    if (it + 2 < n_it) issue(it + 2, q0, o0, ls0, dl0);
-    step(it + 1, q1, o1, ls1, dl1);
+    if (it + 2 < n_it) issue(p2, q0, o0, ls0, dl0);
+    step(p1, q1, o1, ls1, dl1);
+    p0 = p2;
   }
   if (it < n_it) {
     wait_vm0();
     barrier_keep_loads();
-    step(it, q0, o0, ls0, dl0);
+    step(p0, q0, o0, ls0, dl0);
   }
 
   if (has_keys && key < w.k1) {
