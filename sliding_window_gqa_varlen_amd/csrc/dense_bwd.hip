@@ -543,6 +543,9 @@ __device__ __forceinline__ void dkdv_tile(const u32x4* qb, const u32x4* ob, cons
   constexpr int DPS = 32 / NV;  // dS elements per dV slot
   constexpr int kAhead = D == 64 ? kBwdAhead64 : kBwdAhead;
   static_assert(32 % NS == 0 && 32 % NV == 0 && NS >= 8, "slot shares");
+  // MASK: query - key = d is allowed iff 0 <= d < eoff and d < W (W > 0): one unsigned compare
+  // against lim (negative d wraps above it); a lane with no valid key (eoff <= 0) allows nothing
+  const unsigned lim = (unsigned)max(0, W ? min(eoff, W) : eoff);
   bf16x8 frag[NF];
   auto read = [&](int f) {
     if (f < 2 * NS) {  // S (f < NS) or dP: query block f & 1, k-step (f % NS) >> 1
@@ -592,7 +595,7 @@ __device__ __forceinline__ void dkdv_tile(const u32x4* qb, const u32x4* ob, cons
       float pr = fast_exp2(__builtin_fmaf(sc[bb][a], c2, l4[x >> 2][a & 3] * -kLog2e));
       if constexpr (MASK) {
         const int d = qoff + 32 * bb + 8 * (a >> 2) + 4 * h2 + (a & 3);  // query - key
-        pr = (d >= 0 && d < eoff && (W == 0 || d < W)) ? pr : 0.f;
+        pr = (unsigned)d < lim ? pr : 0.f;
       }
       sc[bb][a] = pr;
       asm volatile("" : "+v"(sc[bb][a]));  // this slot's probabilities stay in this slot
@@ -816,6 +819,7 @@ __device__ __forceinline__ void dkdv16_tile(const u32x4* qb, const u32x4* ob, co
                                             const int (&toff)[8], float c2, f32x4 (&dk)[8], f32x4 (&dv)[8],
                                             int qoff, int eoff, int W, int g) {
   constexpr int kAhead = kBwdAhead;
+  const unsigned lim = (unsigned)max(0, W ? min(eoff, W) : eoff);  // as in dkdv_tile
   bf16x8 frag[64];
   auto read = [&](int f) {
     if (f < 32) {  // S (f < 16) or dP: query block b = f & 3, k-step s = (f >> 2) & 3
@@ -861,7 +865,7 @@ __device__ __forceinline__ void dkdv16_tile(const u32x4* qb, const u32x4* ob, co
     float pr = fast_exp2(__builtin_fmaf(sc[b][a], c2, l4[b][a] * -kLog2e));
     if constexpr (MASK) {
       const int d = qoff + 16 * b + 4 * g + a;  // query - key
-      pr = (d >= 0 && d < eoff && (W == 0 || d < W)) ? pr : 0.f;
+      pr = (unsigned)d < lim ? pr : 0.f;
     }
     sc[b][a] = pr;
     asm volatile("" : "+v"(sc[b][a]));
