@@ -245,7 +245,7 @@ int32_t varlen_attn_bwd(const swa_tensor* q, const swa_tensor* k, const swa_tens
   p.dv_st = dv->stride[0];
   p.dv_sh = dv->stride[1];
   p.dsinks = sinks != nullptr ? dsinks : nullptr;
-  swa::dense_bwd_plan(p);
+  swa::dense_bwd_plan(p, (int)D);
   if ((int64_t)f.Hkv * f.n_chunks * f.n_vtiles > INT32_MAX / 2 || (int64_t)f.Hkv * p.kv_n_vtiles > INT32_MAX / 2)
     return fail(SWA_ERR_UNSUPPORTED, "problem too large for one launch");
   const hipError_t e = swa::dense_bwd_launch(p, (int)D, reinterpret_cast<hipStream_t>(stream));

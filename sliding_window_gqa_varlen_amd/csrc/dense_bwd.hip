@@ -21,8 +21,9 @@
 //    Its prologue computes delta = <dout, out> of the lane's column (the two half-waves each
 //    hold half the coordinates) and writes it for the dk/dv and dsink kernels, which run after;
 //    its dq tile leaves through the idle LDS buffer pair so every store writes whole rows.
-//  * dk/dv kernel (key-parallel): a workgroup owns 128 keys of one KV head (32 per wave with
-//    32x32 MFMAs for head_dim 64, 16 per wave of 8 waves with 16x16x32 MFMAs for head_dim 128;
+//  * dk/dv kernel (key-parallel): a workgroup owns the keys of one KV head (head_dim 64: 64 keys,
+//    32 per wave of 2 waves with 32x32 MFMAs; head_dim 128: 128 keys, 16 per wave of 8 waves with
+//    16x16x32 MFMAs;
 //    their K and V rows held in registers) and walks the 64-query tiles of every query head
 //    of the group that can see them.  S = Q K^T and dP = dO V^T (queries = M, keys = N),
 //    so the lane of a key column holds P and dS in the B-operand layout of
@@ -44,7 +45,7 @@
 namespace swa {
 namespace {
 
-constexpr int kTK = 128;           // keys per dk/dv workgroup
+constexpr int kDkdvWaves64 = 2;    // waves of a head_dim-64 dk/dv workgroup (32 keys each)
 constexpr int kBwdAhead = 8;    // dk/dv operand fragments read this many MFMAs ahead (head_dim 128)
 constexpr int kBwdAhead64 = 4;  // the same for head_dim 64
 constexpr int kDqOcc64 = 3;     // head_dim 64 dq: 3 waves / SIMD (168 VGPRs, 2 dwords spilled outside the loop)
@@ -83,21 +84,24 @@ __device__ __forceinline__ uint32_t rows64_lane_off(int64_t st, int lane, int wa
 }
 
 // 64 rows (r0 .. r0 + 63, clamped to r_last >= r0) of D bf16 each into buf; logical unit u of
-// row r lands at physical unit u ^ key(r).  U / 4 transfers of 64 units per wave.  A full tile
-// takes the lane offset from rows64_lane_off and costs no VALU; a clamped (last) tile
-// recomputes every row.
-template <int D, bool RT>
+// row r lands at physical unit u ^ key(r).  U / NW transfers of 64 units per wave (NW waves
+// share the tile).  A full tile takes the lane offset from rows64_lane_off and costs no VALU; a
+// clamped (last) tile recomputes every row.
+template <int D, bool RT, int NW = 4>
 __device__ __forceinline__ void dma_rows64(const __bf16* base, int64_t st, int r0, int r_last, u32x4* buf, int wave,
                                            int lane_in, uint32_t lane_off) {
   constexpr int U = Bw<D>::U, R = 64 / U;  // rows per 64-unit block
+  // the lane offset is the same for every transfer when the key's row bits stay within the
+  // wave's block of rows: true for NW = 4, and for NW = 2 at head_dim 64 (checked on the host)
+  static_assert(NW == 4 || (NW == 2 && D == 64), "lane offset not invariant");
   const __amdgpu_buffer_rsrc_t rsrc =
       __builtin_amdgcn_make_buffer_rsrc((void*)(base + (int64_t)r0 * st), (short)0, -1, kBufferWord3);
   const uint32_t stb = (uint32_t)st * 2u;
   const int lim = r_last - r0;
   if (lim >= 63) {
 #pragma unroll
-    for (int i = 0; i < U / 4; ++i) {
-      const int blk = i * 4 + wave;
+    for (int i = 0; i < U / NW; ++i) {
+      const int blk = i * NW + wave;
       u32x4* dst = buf + __builtin_amdgcn_readfirstlane(blk * 64);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)dst, 16, lane_off,
                                                __builtin_amdgcn_readfirstlane((uint32_t)(blk * R) * stb), 0, 0);
@@ -107,8 +111,8 @@ __device__ __forceinline__ void dma_rows64(const __bf16* base, int64_t st, int r
   const int lane = opaque(lane_in);
   const int lr = lane / U, lp = lane % U;
 #pragma unroll
-  for (int i = 0; i < U / 4; ++i) {
-    const int blk = i * 4 + wave;  // wave-uniform block of R rows
+  for (int i = 0; i < U / NW; ++i) {
+    const int blk = i * NW + wave;  // wave-uniform block of R rows
     const int r = blk * R + lr;
     const int cu = lp ^ (RT ? rt_key<D>(r) : row_key<D>(r));
     u32x4* dst = buf + __builtin_amdgcn_readfirstlane(blk * 64);
@@ -367,25 +371,26 @@ __device__ __forceinline__ int wave_sum(int x) {
 }
 
 // Rank r of the head's key tiles, heaviest first, when the segments fit a wave's lanes
-// (n_docs + 2 <= 64).  The query tiles a key tile walks are ceil(min(R, 127 + W) / 64) (R = keys
-// from the tile to the document end; no cap without a window), non-increasing along a document,
-// so the tiles of a document with at least x query tiles are its first
-// min(n_tiles, ceil((len - 64 (x - 1)) / 128)).  A binary search on x over the lane-wise counts
-// finds the weight of rank r; ties go in document order.  Padding segments come last.
-__device__ __forceinline__ bool decode_heavy_first(const DenseFwdParams& f, int r, KeyTile& w) {
+// (n_docs + 2 <= 64).  The query tiles a key tile of TK keys walks are
+// ceil(min(R, TK - 1 + W) / 64) (R = keys from the tile to the document end; no cap without a
+// window), non-increasing along a document, so the tiles of a document with at least x query
+// tiles are its first min(n_tiles, ceil((len - 64 (x - 1)) / TK)).  A binary search on x over the
+// lane-wise counts finds the weight of rank r; ties go in document order.  Padding segments come
+// last.
+__device__ __forceinline__ bool decode_heavy_first(const DenseFwdParams& f, int r, int TK, KeyTile& w) {
   const int lane = threadIdx.x & 63;
   const int nseg = f.n_docs + 2;
   const bool seg_ok = lane < nseg;
   const int st = seg_ok ? seg_bound(f, lane) : 0;
   const int en = seg_ok ? seg_bound(f, lane + 1) : 0;
   const int len = en - st;
-  const int nt = (len + kTK - 1) / kTK;
+  const int nt = (len + TK - 1) / TK;
   const bool real = seg_ok && lane >= 1 && lane <= f.n_docs;
-  const int cap = f.window ? 127 + f.window : INT_MAX;
+  const int cap = f.window ? TK - 1 + f.window : INT_MAX;
   auto count_ge = [&](int x) -> int {
     const int need = 64 * (x - 1);
     if (!real || cap <= need || len <= need) return 0;
-    return min(nt, (len - need + kTK - 1) / kTK);
+    return min(nt, (len - need + TK - 1) / TK);
   };
   const int n_real = __builtin_amdgcn_readfirstlane(wave_sum(real ? nt : 0));
   int seg, t;
@@ -427,12 +432,12 @@ __device__ __forceinline__ bool decode_heavy_first(const DenseFwdParams& f, int 
   }
   w.seg_start = __builtin_amdgcn_readlane(st, seg);
   w.seg_end = __builtin_amdgcn_readlane(en, seg);
-  w.k0 = w.seg_start + t * kTK;
-  w.k1 = min(w.k0 + kTK, w.seg_end);
+  w.k0 = w.seg_start + t * TK;
+  w.k1 = min(w.k0 + TK, w.seg_end);
   return true;
 }
 
-// blockIdx -> (KV head, 128-key tile of a segment); each KV head's tiles on one XCD, heaviest
+// blockIdx -> (KV head, key tile of a segment); each KV head's tiles on one XCD, heaviest
 // first (the tail of a launch is then made of light tiles).  With more than 62 documents: each
 // document's tiles first-first (under a causal mask the first keys are seen by the most queries).
 // Workgroups reach the XCDs round-robin (x = blockIdx % 8, j = blockIdx / 8 is the order within
@@ -465,17 +470,18 @@ __device__ __forceinline__ bool decode_key_tile(const DenseBwdParams& p, KeyTile
   const DenseFwdParams& f = p.f;
   int v;
   if (!key_tile_slot(p, w.g, v)) return false;
-  if (p.kv_heavy_first) return decode_heavy_first(f, v, w);
+  const int TK = p.kv_tile;
+  if (p.kv_heavy_first) return decode_heavy_first(f, v, TK, w);
   int lo = 0, hi = f.n_docs + 2;
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
-    if (seg_bound(f, mid) / kTK + mid <= v) lo = mid; else hi = mid;
+    if (seg_bound(f, mid) / TK + mid <= v) lo = mid; else hi = mid;
   }
   w.seg_start = seg_bound(f, lo);
   w.seg_end = seg_bound(f, lo + 1);
-  w.k0 = w.seg_start + (v - (w.seg_start / kTK + lo)) * kTK;
+  w.k0 = w.seg_start + (v - (w.seg_start / TK + lo)) * TK;
   if (w.k0 >= w.seg_end) return false;
-  w.k1 = min(w.k0 + kTK, w.seg_end);
+  w.k1 = min(w.k0 + TK, w.seg_end);
   w.padding = (lo == 0 || lo == f.n_docs + 1);
   return true;
 }
@@ -631,7 +637,9 @@ __device__ __forceinline__ void dkdv_tile(const u32x4* qb, const u32x4* ob, cons
 }
 
 template <int D>
-__global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void bwd_dkdv_kernel(DenseBwdParams p) {
+__global__ __launch_bounds__(64 * kDkdvWaves64, 2) void bwd_dkdv_kernel(DenseBwdParams p) {
+  static_assert(D == 64, "head_dim 128 uses bwd_dkdv16_kernel");
+  constexpr int NW = kDkdvWaves64;
   using B = Bw<D>;
   __shared__ u32x4 q0[B::TileUnits];
   __shared__ u32x4 q1[B::TileUnits];
@@ -648,7 +656,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void bwd_dkdv_kernel(Den
   if (!decode_key_tile(p, w)) return;
   if (w.padding) {  // keys outside every document receive no gradient
     const int n_rows = w.k1 - w.k0;
-    for (int idx = threadIdx.x; idx < n_rows * B::U; idx += kThreads) {
+    for (int idx = threadIdx.x; idx < n_rows * B::U; idx += 64 * NW) {
       const int row = idx / B::U, cu = idx - row * B::U;
       const int64_t t = w.k0 + row;
       *(u32x4*)((__bf16*)p.dk + t * p.dk_st + (int64_t)w.g * p.dk_sh + cu * 8) = u32x4{0, 0, 0, 0};
@@ -696,8 +704,9 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void bwd_dkdv_kernel(Den
   auto issue = [&](const WalkPos& wp, u32x4* qb, u32x4* ob, float* lb, float* db) {
     const int h = w.g * f.G + wp.head;
     const int i0 = w.k0 + 64 * wp.tile;
-    dma_rows64<D, true>((const __bf16*)f.q + (int64_t)h * f.q_sh, f.q_st, i0, i_hi - 1, qb, wave, lane, qoff_l);
-    dma_rows64<D, true>((const __bf16*)p.dout + (int64_t)h * p.do_sh, p.do_st, i0, i_hi - 1, ob, wave, lane, ooff_l);
+    dma_rows64<D, true, NW>((const __bf16*)f.q + (int64_t)h * f.q_sh, f.q_st, i0, i_hi - 1, qb, wave, lane, qoff_l);
+    dma_rows64<D, true, NW>((const __bf16*)p.dout + (int64_t)h * p.do_sh, p.do_st, i0, i_hi - 1, ob, wave, lane,
+                            ooff_l);
     if (wave == 0) dma_rowvals(f.lse, f.Hq, h, i0, i_hi - 1, lb, lane);
     if (wave == 1) dma_rowvals(p.delta, f.Hq, h, i0, i_hi - 1, db, lane);
   };
@@ -1025,9 +1034,10 @@ __global__ __launch_bounds__(kT16, 1) void bwd_dkdv16_kernel(DenseBwdParams p) {
 
 }  // namespace
 
-void dense_bwd_plan(DenseBwdParams& p) {
+void dense_bwd_plan(DenseBwdParams& p, int D) {
   dense_fwd_plan(p.f);
-  p.kv_n_vtiles = p.f.T / kTK + p.f.n_docs + 2;
+  p.kv_tile = D == 64 ? 32 * kDkdvWaves64 : 128;
+  p.kv_n_vtiles = p.f.T / p.kv_tile + p.f.n_docs + 2;
   p.kv_n_work = p.f.Hkv * p.kv_n_vtiles;
   // heavy-first key tiles where the causal mask makes their weights uneven (segments must fit
   // the lanes of one wave)
@@ -1050,7 +1060,7 @@ hipError_t bwd_launch(const DenseBwdParams& p, hipStream_t stream) {
     if constexpr (D == 128)
       hipLaunchKernelGGL(bwd_dkdv16_kernel, dim3((unsigned)gk), dim3(kT16), 0, stream, p);
     else
-      hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3((unsigned)gk), dim3(kThreads), 0, stream, p);
+      hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3((unsigned)gk), dim3(64 * kDkdvWaves64), 0, stream, p);
   }
   if (p.f.sinks != nullptr && p.dsinks != nullptr) {
     const unsigned n_chunks = (unsigned)((p.f.T + kSinkChunk - 1) / kSinkChunk);

@@ -51,13 +51,14 @@ struct DenseBwdParams {
   void* dv;
   int64_t dv_st, dv_sh;
   float* dsinks;        // [Hq] or null (written when f.sinks is set)
-  int32_t kv_n_vtiles;  // virtual 128-key tiles per KV head
+  int32_t kv_tile;      // keys per dk/dv workgroup: 64 (head_dim 64) or 128 (head_dim 128)
+  int32_t kv_n_vtiles;  // virtual key tiles per KV head
   int32_t kv_n_work;    // Hkv * kv_n_vtiles
   int32_t kv_heavy_first;  // key tiles in heavy-first order (set by dense_bwd_plan)
 };
 
-// Fills the key-tile plan (and, through dense_fwd_plan, the query-tile plan) of p.
-void dense_bwd_plan(DenseBwdParams& p);
+// Fills the key-tile plan for head_dim D (and, through dense_fwd_plan, the query-tile plan) of p.
+void dense_bwd_plan(DenseBwdParams& p, int D);
 hipError_t dense_bwd_launch(const DenseBwdParams& p, int D, hipStream_t stream);
 
 // Sparse MLA forward (bf16). Strides in elements.

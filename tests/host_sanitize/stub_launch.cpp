@@ -24,7 +24,12 @@ hipError_t dense_fwd_launch(const DenseFwdParams&, Dtype, int, hipStream_t) {
   ++g_launches;
   return hipSuccess;
 }
-void dense_bwd_plan(DenseBwdParams& p) { dense_fwd_plan(p.f); }
+void dense_bwd_plan(DenseBwdParams& p, int D) {
+  dense_fwd_plan(p.f);
+  p.kv_tile = D == 64 ? 64 : 128;  // the fields the size guard reads, as the device plan sets them
+  p.kv_n_vtiles = p.f.T / p.kv_tile + p.f.n_docs + 2;
+  p.kv_n_work = p.f.Hkv * p.kv_n_vtiles;
+}
 hipError_t dense_bwd_launch(const DenseBwdParams&, int, hipStream_t) {
   ++g_launches;
   return hipSuccess;
