@@ -36,7 +36,10 @@
 //    units.  The output tile leaves through LDS so that every store writes whole rows.
 //  * Online softmax with lazy rescaling: the reference maximum moves only when a score
 //    exceeds it by more than 2^8 (probabilities stay <= 256), so most tiles skip the O
-//    rescale; the final normalisation uses the same reference, so the result is exact.
+//    rescale; the final normalisation uses the same reference, so the result is exact.  The
+//    bf16 kernel takes a tile's maximum only when a lane's partial row sum of the tile
+//    exceeds 2^8 (the sum bounds every probability), which is rare once the first tile has
+//    set the reference.
 //  * fp32 inputs use v_mfma_f32_32x32x2_f32 with the same accumulator layout and a
 //    register-staged, padded LDS layout (parity path, not tuned).
 #include <type_traits>
@@ -47,8 +50,8 @@ namespace swa {
 namespace {
 
 constexpr float kRescaleLog2 = 8.f;  // lazy-rescale threshold (log2 units)
-constexpr int kAhead128 = 8;  // operand fragments read this many MFMAs ahead (head_dim >= 128)
-constexpr int kAhead64 = 4;   // the same for head_dim 64
+constexpr int kAhead128 = 6;  // operand fragments read this many MFMAs ahead (head_dim >= 128)
+constexpr int kAhead64 = 2;   // the same for head_dim 64
 constexpr int kOcc64 = 3;     // head_dim 64: three workgroups per CU
 
 template <typename T, int D>
@@ -102,36 +105,38 @@ __device__ __forceinline__ float lane_max(const f32x16 (&sc)[2]) {
   return mx;
 }
 
-__device__ __forceinline__ float block_max(const f32x16& b) {
-  float mx = -INFINITY;
-#pragma unroll
-  for (int a = 0; a < 16; ++a) mx = fmaxf(mx, b[a]);
-  return mx;
+// What the pipelined loop keeps of the statistics between tiles: the exponent offset of the
+// probabilities, and the largest partial row sum that shows the reference may stay.  A lane's
+// 32 probabilities of a tile that sum to at most 2^8 are each at most 2^8, so the maximum of its
+// scores lies at most 8 (log2 units) above the reference and tile_stats would keep it (up to the
+// rounding of that comparison, where either choice gives the exact result).  The maximum is then
+// needed only when a sum exceeds the bound: rarely, once the first tile has set the reference.
+// While the reference is -inf (nothing visible yet) the bound is -1, so every tile takes the
+// exact path until something is visible.
+constexpr float kLazyMax = 256.f;  // 2^kRescaleLog2
+struct Lazy {
+  float mu, thr;
+};
+__device__ __forceinline__ Lazy lazy_of(const Softmax& st, const TileStats& t) {
+  return Lazy{t.mu, st.mref == -INFINITY ? -1.f : kLazyMax};
 }
 
-// Masks a diagonal / window-edge tile block by block and returns the lane maximum of what is
-// left (head_dim 256, whose one wave per SIMD has no other wave to hide the masking behind).
-// A block that needs no mask keeps its maximum (m[blk] when HaveMax, else computed); a block
-// that no query of the wave sees (all keys after the wave's last token, or all before its
-// first token's window) is set to -inf without per-score tests; only a block that the cut
-// crosses is masked score by score and its maximum taken again.
-template <bool HaveMax>
-__device__ __forceinline__ float mask_tile_max(f32x16 (&sc)[2], int kb, const Cols& c, const float (&m)[2]) {
+// Masks a diagonal / window-edge tile block by block (head_dim 256, whose one wave per SIMD has
+// no other wave to hide the masking behind).  A block that needs no mask is left alone; a block
+// that no query of the wave sees (all keys after the wave's last token, or all before its first
+// token's window) is set to -inf without per-score tests; only a block that the cut crosses is
+// masked score by score.
+__device__ __forceinline__ void mask_tile_blocks(f32x16 (&sc)[2], int kb, const Cols& c) {
   const int tq4 = opaque(c.tq - 4 * c.h2);  // as in mask_tile
   const int lo = c.W ? tq4 - c.W + 1 - kb : -(1 << 30);
   const unsigned range = (unsigned)(tq4 - kb - lo);
-  float mx[2];
 #pragma unroll
   for (int blk = 0; blk < 2; ++blk) {
     const int b0 = kb + 32 * blk;
-    if (!(b0 + 31 > c.tw0 || (c.W != 0 && b0 <= c.tw1 - c.W))) {
-      mx[blk] = HaveMax ? m[blk] : block_max(sc[blk]);
-      continue;
-    }
+    if (!(b0 + 31 > c.tw0 || (c.W != 0 && b0 <= c.tw1 - c.W))) continue;
     if (b0 > c.tw1 || (c.W != 0 && b0 + 31 <= c.tw0 - c.W)) {
 #pragma unroll
       for (int a = 0; a < 16; ++a) sc[blk][a] = -INFINITY;
-      mx[blk] = -INFINITY;
       continue;
     }
 #pragma unroll
@@ -139,9 +144,23 @@ __device__ __forceinline__ float mask_tile_max(f32x16 (&sc)[2], int kb, const Co
       const int off = 32 * blk + 8 * (a >> 2) + (a & 3);
       sc[blk][a] = (unsigned)(off - lo) <= range ? sc[blk][a] : -INFINITY;
     }
-    mx[blk] = block_max(sc[blk]);
   }
-  return fmaxf(mx[0], mx[1]);
+}
+
+// Probabilities exp2(s c2 - mu) of the lane's scores as the four B operands of O^T += V^T P^T,
+// and their sum, added in the order of the pipelined step.
+__device__ __forceinline__ float tile_probs(const f32x16 (&sc)[2], float c2, float mu, bf16x8 (&pb)[4]) {
+  float rs = 0.f;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    f32x8 pf;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pf[e] = fast_exp2(__builtin_fmaf(sc[g >> 1][8 * (g & 1) + e], c2, -mu));
+    pb[g] = cvt_bf16x8(pf);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) rs += pf[e];
+  }
+  return rs;
 }
 
 // Scores -> unnormalised probabilities exp2(s * c2 - mu), in place; returns their sum.
@@ -383,25 +402,23 @@ __device__ __forceinline__ void pv_tile(const u32x4* vbuf, const f32x16 (&sc)[2]
 }
 
 // One pipelined step in program order: S(j) = K(j) Q^T on the MFMA unit while the
-// exponentials of tile j-1 run on the VALU, then O += V(j-1) P(j-1).  For head_dim 128 the
-// last 8 exponentials of a lane (the B operand of the last PV k-step) run in the PV slots
-// before that k-step instead, which evens out the VALU work between the two halves of the
-// step (a wave64 VALU op issues in 4 cycles, an exponential in 8, and a 32x32x16 MFMA keeps
-// the VALU from issuing for about half of its 32 cycles; measured 1-1.5 % faster, while head_dim
-// 256 ran 3 % slower and keeps the plain order).  Operand fragments
-// stream from LDS kAhead MFMAs ahead of their use (K fragments first, then the transposed
-// V fragments), so each MFMA waits only for a read issued long before.  Every slot is
-// fenced with sched_barrier: the emitted order is exactly this one.
-template <int D>
+// exponentials of tile j-1 run on the VALU (a wave64 VALU op issues in 4 cycles, an exponential
+// in 8, and a 32x32x16 MFMA keeps the VALU from issuing for about half of its 32 cycles), then
+// O += V(j-1) P(j-1).  Between the two halves one compare of the lane's partial row sum against
+// lz.thr decides, for the whole wave, whether the rare exact path `move` runs: it takes the
+// tile's maximum, moves the reference where tile_stats says so, rescales O and recomputes the
+// probabilities (pb) and their sum, which it returns.  Operand fragments stream from LDS kAhead
+// MFMAs ahead of their use (K fragments first, then the transposed V fragments), so each MFMA
+// waits only for a read issued long before.  Every slot is fenced with sched_barrier: the
+// emitted order is exactly this one.
+template <int D, class Move>
 __device__ __forceinline__ float qk_pv_step(const u32x4* kbuf, const u32x4* vbuf, const bf16x8 (&qf)[Bf<D>::kQFrags],
                                             int kaddr, const VOffsets<D>& vo, f32x16 (&sn)[2],
-                                            const f32x16 (&sc)[2], float c2, float mu, f32x16 (&o)[Bf<D>::kDBlocks],
-                                            float (&sn_max)[2]) {
+                                            const f32x16 (&sc)[2], float c2, const Lazy& lz,
+                                            f32x16 (&o)[Bf<D>::kDBlocks], Move&& move) {
   using B = Bf<D>;
   constexpr int NQ = 2 * B::kQFrags;  // QK^T MFMAs (32 for D = 256, 16 for D = 128, 8 for D = 64)
   constexpr int NP = 4 * B::kDBlocks; // PV MFMAs
-  constexpr int KS = D == 128 ? 24 : 32;  // exponentials in the QK^T slots; the rest run in PV slots
-  constexpr int NP3 = 3 * NP / 4;          // PV slots before the last k-step
   constexpr int kAhead = (D >= 128) ? kAhead128 : kAhead64;
   u32x4 frag[NQ + NP];
   __builtin_amdgcn_s_setprio(1);  // the wave in its MFMA stream goes first
@@ -426,53 +443,42 @@ __device__ __forceinline__ float qk_pv_step(const u32x4* kbuf, const u32x4* vbuf
   float rs = 0.f;
   // exponential x of tile j-1 (block x / 16, accumulator x % 16); every 8 form a B operand
   auto exp_step = [&](int x) {
-    pf[x & 7] = fast_exp2(__builtin_fmaf(sc[x >> 4][x & 15], c2, -mu));
+    pf[x & 7] = fast_exp2(__builtin_fmaf(sc[x >> 4][x & 15], c2, -lz.mu));
     asm volatile("" : "+v"(pf[x & 7]));  // this slot's exponentials stay in this slot
     if ((x & 7) == 7) {
       pb[x >> 3] = cvt_bf16x8(pf);
+      // packed here: otherwise the conversion, common to both paths after the check, sinks
+      // below it and keeps the 8 fp32 values live instead of 4 packed registers
+      asm volatile("" : "+v"(pb[x >> 3]));
 #pragma unroll
       for (int h = 0; h < 8; ++h) rs += pf[h];
     }
   };
+  // head_dim 256 (one wave per SIMD, nothing to hide a stall behind) finishes its exponentials
+  // two QK^T slots early, so the sum, the compare and the branch run under MFMAs already issued
+  constexpr int QX = NQ - (D == 256 ? 2 : 0);  // QK^T slots that carry exponentials
 #pragma unroll
-  for (int i = 0; i < NQ; ++i) {
+  for (int i = 0; i < QX; ++i) {
     sn[i & 1] = mfma_bf16_32x32x16(__builtin_bit_cast(bf16x8, frag[i]), qf[i >> 1], sn[i & 1]);
     if (i + kAhead < NQ + NP) read(i + kAhead);
 #pragma unroll
-    for (int x = KS * i / NQ; x < KS * (i + 1) / NQ; ++x) exp_step(x);
+    for (int x = 32 * i / QX; x < 32 * (i + 1) / QX; ++x) exp_step(x);
     __builtin_amdgcn_sched_barrier(0);
   }
-  if constexpr (KS == 32) asm volatile("" ::"v"(rs));  // the row sum is finished inside the stream
-  // the 16 max steps (two new scores each) over the NP PV slots: steps [16 i / NP, 16 (i + 1) / NP).
-  // head_dim 256 keeps one maximum per 32-key block (a masked tile takes again only a masked
-  // block's); the others one maximum in sn_max[0]
-  constexpr int NC = D == 256 ? 2 : 1;
-  float mx[2] = {-INFINITY, -INFINITY};
+  if (__builtin_amdgcn_ballot_w64(!(rs <= lz.thr)) != 0) rs = move(pb);
+#pragma unroll
+  for (int i = QX; i < NQ; ++i) {
+    sn[i & 1] = mfma_bf16_32x32x16(__builtin_bit_cast(bf16x8, frag[i]), qf[i >> 1], sn[i & 1]);
+    if (i + kAhead < NQ + NP) read(i + kAhead);
+    __builtin_amdgcn_sched_barrier(0);
+  }
 #pragma unroll
   for (int i = 0; i < NP; ++i) {
     const int ks = i / B::kDBlocks, d = i % B::kDBlocks;
     o[d] = mfma_bf16_32x32x16(__builtin_bit_cast(bf16x8, frag[NQ + i]), pb[ks], o[d]);
     if (NQ + i + kAhead < NQ + NP) read(NQ + i + kAhead);
-    if constexpr (KS < 32) {
-      if (i < NP3) {
-#pragma unroll
-        for (int x = KS + (32 - KS) * i / NP3; x < KS + (32 - KS) * (i + 1) / NP3; ++x) exp_step(x);
-      }
-    }
-#pragma unroll
-    for (int e = 16 * i / NP; e < 16 * (i + 1) / NP; ++e) {
-      const int x = 2 * e;
-      const int ch = NC == 2 ? x >> 4 : 0;
-      mx[ch] = fmaxf(mx[ch], sn[x >> 4][x & 15]);
-      mx[ch] = fmaxf(mx[ch], sn[x >> 4][(x & 15) + 1]);
-    }
-    asm volatile("" : "+v"(mx[0]));  // keeps this slot's share of the maximum in this slot
-    if constexpr (NC == 2) asm volatile("" : "+v"(mx[1]));
     __builtin_amdgcn_sched_barrier(0);
   }
-  if constexpr (KS < 32) asm volatile("" ::"v"(rs));
-  sn_max[0] = mx[0];
-  sn_max[1] = mx[1];
   __builtin_amdgcn_s_setprio(0);
   return rs;
 }
@@ -529,45 +535,47 @@ __global__ __launch_bounds__(kThreads, D == 64 ? kOcc64 : D == 128 ? 2 : 1) void
   barrier_keep_loads();
   f32x16 sc[2];
   qk_tile<D>(k0, qf, c.n, c.h2, sc);
-  float s0_max;
-  if constexpr (D == 256) {
-    const float no_max[2] = {-INFINITY, -INFINITY};
-    s0_max = tile_needs_mask(c, c.k_lo) ? mask_tile_max<false>(sc, c.k_lo, c, no_max) : lane_max(sc);
-  } else {
-    if (tile_needs_mask(c, c.k_lo)) mask_tile(sc, c.k_lo, c);
-    s0_max = lane_max(sc);
+  if (tile_needs_mask(c, c.k_lo)) {
+    if constexpr (D == 256) mask_tile_blocks(sc, c.k_lo, c);
+    else mask_tile(sc, c.k_lo, c);
   }
-  TileStats ts = tile_stats(s0_max, c2, st);
+  // the first tile sets the reference (O and l are still zero: nothing to rescale)
+  Lazy lz;
+  {
+    const TileStats t0 = tile_stats(lane_max(sc), c2, st);
+    lz = lazy_of(st, t0);
+  }
+  // the exact path of a tile whose probabilities may exceed 2^8 (scores of the tile in sc)
+  auto exact = [&](float& alpha) {
+    const TileStats t = tile_stats(lane_max(sc), c2, st);
+    rescale_o<B::kDBlocks>(t.move, t.alpha, o);
+    lz = lazy_of(st, t);
+    alpha = t.alpha;
+  };
 
   // iteration j: S(j) from K(j) ; softmax + PV of tile j-1 ; K(j+1), V(j) in flight.
-  // On entry sc holds the masked scores of tile j-1 and ts their statistics.  After the
-  // rare O rescale, one fenced instruction stream runs the QK^T MFMAs of tile j with the
-  // exponentials of tile j-1 between them, masks tile j if it straddles the diagonal or
-  // the window edge, then runs the PV MFMAs of tile j-1 with the maximum of tile j between
-  // them.  Tiles a wave does not see are computed too: fully masked, they add nothing.
+  // On entry sc holds the masked scores of tile j-1 and lz the offset of their probabilities.
+  // One fenced instruction stream runs the QK^T MFMAs of tile j with the exponentials of tile
+  // j-1 between them, then (after the rare exact path) the PV MFMAs of tile j-1; tile j is then
+  // masked if it straddles the diagonal or the window edge.  Tiles a wave does not see are
+  // computed too: fully masked, they add nothing.
   auto step = [&](int j, const u32x4* kcur, u32x4* knext, u32x4* vcur_dst, const u32x4* vprev) {
     const int kb = c.k_lo + j * kBN;
     wait_vm0();
     barrier_keep_loads();  // K(j), V(j-1) landed for every wave; K(j-1), V(j-2) consumed
     if (j + 1 < nt) dma_tile<D, false>(kbase, p.k_st, kb + kBN, c.k_hi, knext, c.wave, c.lane, kdl);
     dma_tile<D, true>(vbase, p.v_st, kb, c.k_hi, vcur_dst, c.wave, c.lane, vdl);
-    rescale_o<B::kDBlocks>(ts.move, ts.alpha, o);
     f32x16 sn[2];
-    float bm[2];
-    const float rs = qk_pv_step<D>(kcur, vprev, qf, kaddr, vo, sn, sc, c2, ts.mu, o, bm);
-    // diagonal / window-edge tile: mask, then take the maximum again
-    float sn_max;
-    if constexpr (D == 256) {
-      sn_max = tile_needs_mask(c, kb) ? mask_tile_max<true>(sn, kb, c, bm) : fmaxf(bm[0], bm[1]);
-    } else {
-      sn_max = bm[0];
-      if (tile_needs_mask(c, kb)) {
-        mask_tile(sn, kb, c);
-        sn_max = lane_max(sn);
-      }
+    float alpha = 1.f;
+    const float rs = qk_pv_step<D>(kcur, vprev, qf, kaddr, vo, sn, sc, c2, lz, o, [&](bf16x8 (&pb)[4]) {
+      exact(alpha);
+      return tile_probs(sc, c2, lz.mu, pb);
+    });
+    if (tile_needs_mask(c, kb)) {
+      if constexpr (D == 256) mask_tile_blocks(sn, kb, c);
+      else mask_tile(sn, kb, c);
     }
-    st.l = st.l * ts.alpha + rs;
-    ts = tile_stats(sn_max, c2, st);
+    st.l = st.l * alpha + rs;
     sc[0] = sn[0];
     sc[1] = sn[1];
   };
@@ -577,27 +585,46 @@ __global__ __launch_bounds__(kThreads, D == 64 ? kOcc64 : D == 128 ? 2 : 1) void
     step(j + 1, k0, k1, v0, v1);
   }
   if (j < nt) step(j, k1, k0, v1, v0);
-  // last tile: its V is in buffer (nt - 1) & 1.  When its second 32-key block starts after this
-  // wave's last token, mask_tile set all of that block's scores to -inf: their probabilities are
-  // exactly zero, so its exponentials and PV k-steps 2 and 3 are skipped (a uniform branch that
-  // leaves the result unchanged).  Not for D = 256, whose registers the second copy of the
-  // tail would spill.
+  // last tile: its K and V are in buffers (nt - 1) & 1.  When its second 32-key block starts
+  // after this wave's last token, the mask set all of that block's scores to -inf: their
+  // probabilities are exactly zero, so its exponentials and PV k-steps 2 and 3 are skipped (a
+  // uniform branch that leaves the result unchanged).  Not for D = 256, whose registers the
+  // second copy of the tail would spill.  The probabilities replace the scores in place; if the
+  // exact path is needed, the scores are computed again from the K tile, which no transfer
+  // overwrites after the last step, and Q read again (the same MFMAs: the same scores).
   wait_vm0();
   barrier_keep_loads();
-  rescale_o<B::kDBlocks>(ts.move, ts.alpha, o);
+  const bool last_odd = (nt - 1) & 1;
+  auto last_tile = [&](auto nb) {
+    constexpr int NB = decltype(nb)::value;
+    float rs = tile_exp<NB>(sc, c2, lz.mu);
+    float alpha = 1.f;
+    if (__builtin_amdgcn_ballot_w64(!(rs <= lz.thr)) != 0) {
+      const Cols cr = fresh_lane_cols(c, p.hb_shift, w);
+      bf16x8 qr[B::kQFrags];
+      const __bf16* qb = (const __bf16*)p.q + (int64_t)min(cr.tq, w.t_end - 1) * p.q_st + (int64_t)cr.hq * p.q_sh;
+#pragma unroll
+      for (int s = 0; s < B::kQFrags; ++s) qr[s] = *(const bf16x8*)(qb + 16 * s + 8 * cr.h2);
+      qk_tile<D>(last_odd ? k1 : k0, qr, cr.n, cr.h2, sc);
+      const int kb = c.k_lo + (nt - 1) * kBN;
+      if (tile_needs_mask(cr, kb)) {
+        if constexpr (D == 256) mask_tile_blocks(sc, kb, cr);
+        else mask_tile(sc, kb, cr);
+      }
+      exact(alpha);
+      rs = tile_exp<NB>(sc, c2, lz.mu);
+    }
+    st.l = st.l * alpha + rs;
+    if (last_odd) pv_tile<D, 2 * NB>(v1, sc, vo, o);
+    else pv_tile<D, 2 * NB>(v0, sc, vo, o);
+  };
   const bool tail_half = D != 256 && c.k_lo + (nt - 1) * kBN + 32 > c.tw1;
-  if (tail_half) {
-    st.l = st.l * ts.alpha + tile_exp<1>(sc, c2, ts.mu);
-    if ((nt - 1) & 1) pv_tile<D, 2>(v1, sc, vo, o);
-    else pv_tile<D, 2>(v0, sc, vo, o);
-  } else {
-    st.l = st.l * ts.alpha + tile_exp(sc, c2, ts.mu);
-    if ((nt - 1) & 1) pv_tile<D>(v1, sc, vo, o);
-    else pv_tile<D>(v0, sc, vo, o);
-  }
-  // every wave is past its last K read (the barrier above): the K buffers hold the output
-  // images, two waves per buffer
-  char* img = (char*)(c.wave < 2 ? k0 : k1) + (c.wave & 1) * (64 * D);
+  if (tail_half) last_tile(std::integral_constant<int, 1>{});
+  else last_tile(std::integral_constant<int, 2>{});
+  // the output images, two waves per buffer, go to the K and V buffers the last tile does not
+  // use: every wave finished reading them before the barrier above and no transfer targets them,
+  // while the last tile's K may still be read by a wave on its exact path and its V by the PV
+  char* img = (char*)(c.wave < 2 ? (last_odd ? k0 : k1) : (last_odd ? v0 : v1)) + (c.wave & 1) * (64 * D);
   const Cols ce = fresh_lane_cols(c, p.hb_shift, w);
   const float inv = epilogue_scalars(p, w, ce, st);
   store_out_bf16<D>(p.out, p.o_st, p.o_sh, w, ce, p.hb_shift, inv, o, img);

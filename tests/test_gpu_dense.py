@@ -202,7 +202,7 @@ def test_many_documents_both_segment_decodes(gpu, n_docs, D, window):
     assert np.all(out[:7] == 0) and np.all(np.isneginf(lse[:7]))
 
 
-@pytest.mark.parametrize("D,window,sinks", [(128, 0, False), (64, 0, True), (128, 300, True)])
+@pytest.mark.parametrize("D,window,sinks", [(128, 0, False), (64, 0, True), (128, 300, True), (256, 0, False)])
 def test_scores_growing_along_the_keys(gpu, D, window, sinks):
     """Every query's scores grow by 0.08 to 0.11 per key (5 to 7 per 64-key tile), so the
     running maximum keeps moving: the lazy reference is exceeded by more than 2^8 every few
@@ -214,6 +214,25 @@ def test_scores_growing_along_the_keys(gpu, D, window, sinks):
     # q . k = D * 0.01 * pos (+ noise); times scale = D^-1/2 the score grows by 0.01 sqrt(D) per key
     q = np.broadcast_to(u, (T, 8, D)) + 0.05 * inp["q"]
     k = (0.01 * pos)[:, None, None] * np.broadcast_to(u, (T, 2, D)) + 0.05 * inp["k"]
+    inp["q"] = W.round_to_bf16(np.ascontiguousarray(q, np.float32))
+    inp["k"] = W.round_to_bf16(np.ascontiguousarray(k, np.float32))
+    ref_o, ref_l = oracle_full(inp)
+    out, lse = run_dense(inp, "bf16")
+    assert_dense_parity("bf16", out, lse, ref_o, ref_l)
+
+
+@pytest.mark.parametrize("D,Hq,Hkv", [(64, 8, 2), (128, 8, 2), (128, 4, 4), (256, 8, 2)])
+def test_score_jump_in_the_last_key_tile(gpu, D, Hq, Hkv):
+    """Scores are flat except for the last 40 keys of each document, which score about 20 above
+    the rest: the query tiles at a document's end meet them only in their last key tile, so the
+    lazy reference moves there, after the pipelined loop (the last tile's exact path)."""
+    lengths = [300, 200, 170]
+    T = sum(lengths)
+    inp = custom(lengths, T=T, Hq=Hq, Hkv=Hkv, D=D, window=0, dtype="bf16", seed=D + Hq)
+    jump = np.concatenate([(np.arange(n) >= n - 40) for n in lengths]).astype(np.float32) * (20.0 / math.sqrt(D))
+    u = np.ones(D, np.float32)
+    q = np.broadcast_to(u, (T, Hq, D)) + 0.05 * inp["q"]
+    k = jump[:, None, None] * np.broadcast_to(u, (T, Hkv, D)) + 0.05 * inp["k"]
     inp["q"] = W.round_to_bf16(np.ascontiguousarray(q, np.float32))
     inp["k"] = W.round_to_bf16(np.ascontiguousarray(k, np.float32))
     ref_o, ref_l = oracle_full(inp)
