@@ -324,7 +324,8 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_fwd_kernel(SparseMlaPa
   for (int seg = 0; seg < p.topk; seg += kSeg) {
     // ---- compact the valid slots of this segment into s_idx (order preserved)
     __syncthreads();  // previous segment's readers of s_idx and of the buffers are done
-    const int base = seg + threadIdx.x * kSlotsPerThread;
+    const Lane Ls = opaque_lane(L);  // lane values rederived, not kept live across the chunk loop
+    const int base = seg + (L.wave * 64 + Ls.lane) * kSlotsPerThread;
     int vals[kSlotsPerThread];
     uint32_t mask = 0;
     if (my_doc >= 0) {
@@ -342,9 +343,9 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_fwd_kernel(SparseMlaPa
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const int yv = __shfl_up(incl, off);
-      if (L.lane >= off) incl += yv;
+      if (Ls.lane >= off) incl += yv;
     }
-    if (L.lane == 63) s_wtot[L.wave] = incl;
+    if (Ls.lane == 63) s_wtot[L.wave] = incl;
     __syncthreads();
     int woff = 0, nv = 0;
 #pragma unroll
@@ -403,11 +404,14 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_fwd_kernel(SparseMlaPa
   }
 
   // ---- epilogue
-  if (!head_ok) return;
+  // the epilogue's lane values rederived as well
+  const Lane Le = opaque_lane(L);
+  const int head_e = blockIdx.y * kHeadsPerBlock + L.hg * 32 + Le.n;
+  if (head_e >= p.H) return;
   const float lt = half_swap_sum(st.l);
   const bool empty = st.mref == -INFINITY;
   const float inv = empty ? 0.f : 1.f / lt;
-  __bf16* ob = (__bf16*)p.out + (int64_t)t * p.o_st + (int64_t)head * p.o_sh + 256 * L.half;
+  __bf16* ob = (__bf16*)p.out + (int64_t)t * p.o_st + (int64_t)head_e * p.o_sh + 256 * L.half;
 #pragma unroll
   for (int d = 0; d < kDBlocks; ++d)
 #pragma unroll
@@ -415,10 +419,10 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_fwd_kernel(SparseMlaPa
       f32x4 r;
 #pragma unroll
       for (int e = 0; e < 4; ++e) r[e] = o[d][4 * i + e] * inv;
-      *(bf16x4*)(ob + 32 * d + 8 * i + 4 * L.h2) = cvt_bf16x4(r);
+      *(bf16x4*)(ob + 32 * d + 8 * i + 4 * Le.h2) = cvt_bf16x4(r);
     }
-  if (p.lse != nullptr && L.h2 == 0 && L.half == 0)
-    p.lse[(int64_t)t * p.H + head] = empty ? -INFINITY : (st.mref + __builtin_amdgcn_logf(lt)) * kLn2;
+  if (p.lse != nullptr && Le.h2 == 0 && L.half == 0)
+    p.lse[(int64_t)t * p.H + head_e] = empty ? -INFINITY : (st.mref + __builtin_amdgcn_logf(lt)) * kLn2;
 }
 
 }  // namespace
