@@ -221,15 +221,21 @@ def test_scores_growing_along_the_keys(gpu, D, window, sinks):
     assert_dense_parity("bf16", out, lse, ref_o, ref_l)
 
 
-@pytest.mark.parametrize("D,Hq,Hkv", [(64, 8, 2), (128, 8, 2), (128, 4, 4), (256, 8, 2)])
-def test_score_jump_in_the_last_key_tile(gpu, D, Hq, Hkv):
-    """Scores are flat except for the last 40 keys of each document, which score about 20 above
-    the rest: the query tiles at a document's end meet them only in their last key tile, so the
-    lazy reference moves there, after the pipelined loop (the last tile's exact path)."""
+@pytest.mark.parametrize("D,Hq,Hkv,size,where", [(64, 8, 2, 20, "end"), (128, 8, 2, 20, "end"), (128, 4, 4, 20, "end"),
+                                                  (256, 8, 2, 20, "end"), (64, 8, 2, 200, "end"),
+                                                  (128, 8, 2, 200, "end"), (128, 8, 2, 200, "middle"),
+                                                  (64, 8, 2, 200, "middle")])
+def test_score_jump_in_the_last_key_tile(gpu, D, Hq, Hkv, size, where):
+    """Scores are flat except for 40 keys of each document, which score `size` above the rest.
+    At the end of a document, the query tiles there meet them only in their last key tile, so the
+    lazy reference moves after the pipelined loop (the last tile's exact path); in the middle
+    (keys 100-139), inside the loop.  A jump of 200 (288 in log2 units) overflows the fast path's
+    probabilities to inf, which must send the tile to the exact path, not into the output."""
     lengths = [300, 200, 170]
     T = sum(lengths)
     inp = custom(lengths, T=T, Hq=Hq, Hkv=Hkv, D=D, window=0, dtype="bf16", seed=D + Hq)
-    jump = np.concatenate([(np.arange(n) >= n - 40) for n in lengths]).astype(np.float32) * (20.0 / math.sqrt(D))
+    sel = (lambda n: np.arange(n) >= n - 40) if where == "end" else (lambda n: (np.arange(n) >= 100) & (np.arange(n) < 140))
+    jump = np.concatenate([sel(n) for n in lengths]).astype(np.float32) * (size / math.sqrt(D))
     u = np.ones(D, np.float32)
     q = np.broadcast_to(u, (T, Hq, D)) + 0.05 * inp["q"]
     k = jump[:, None, None] * np.broadcast_to(u, (T, Hkv, D)) + 0.05 * inp["k"]
