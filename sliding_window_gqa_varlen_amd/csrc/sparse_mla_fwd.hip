@@ -51,6 +51,7 @@ constexpr int kTokenRun = 64;                       // consecutive tokens per XC
 constexpr int kSlotsPerThread = kSeg / kThreads;    // 4
 constexpr int kDBlocks = 8;                         // 256 output coordinates per wave / 32
 constexpr float kRescaleLog2 = 8.f;                 // lazy-rescale threshold (log2 units)
+constexpr float kLazyMax = 256.f;                   // 2^kRescaleLog2: the fast path's bound on a lane's sum
 constexpr int kQAhead = 3;         // QK^T fragments read ahead of their MFMA
 constexpr int kPvAhead = 2;       // PV fragments read ahead of their MFMA
 static_assert(kLatRegion % (64 * kWaves) == 0 && (kSlots * kRopeUnits * 4) % (64 * kWaves) == 0,
@@ -186,14 +187,35 @@ __device__ __forceinline__ f32x16 qk_partial(const u32x4* buf, const bf16x8* qf,
   return sc;
 }
 
+// Probabilities exp2(s c2 - mu) of the lane's 16 scores as the two B operands of the PV MFMAs,
+// and their sum.
+__device__ __forceinline__ float chunk_probs(const f32x16& sc, float c2, float mu, bf16x8 (&pb)[2]) {
+  float rs = 0.f;
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    f32x8 pf;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pf[e] = fast_exp2(__builtin_fmaf(sc[8 * s + e], c2, -mu));
+    pb[s] = cvt_bf16x8(pf);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) rs += pf[e];
+  }
+  return rs;
+}
+
 // Online softmax over the chunk's full scores, then O^T[d][head] += latent^T[d][slot] P^T[slot][head]
 // over this wave's 256 output coordinates.
+// The probabilities are first taken against the current reference without the chunk's maximum:
+// a lane whose 16 probabilities sum to at most 2^8 has none above 2^8, so its scores lie at most
+// 8 (log2 units) above the reference and the lazy rescale below would keep it (up to the
+// rounding of that comparison, where either choice gives the exact result).  Only when some
+// lane's sum exceeds the bound (or its reference is still -inf: the bound is then -1) does the
+// wave take the exact path: the maximum, the move where it is due, the O rescale and the
+// probabilities again.
 __device__ __forceinline__ void finish_chunk(const u32x4* buf, f32x16 sc, int n_in_chunk, f32x16* o,
                                              SoftmaxState& st, float c2, const Lane& Lw) {
   const Lane L = opaque_lane(Lw);
-  // raw scores; slots past the compacted count are masked.  The log2-unit scale c2 > 0 is
-  // applied to the maximum (rounding is monotone, so max(s) c2 = max(s c2)) and folded into
-  // one fma per score with the exponent offset below.
+  // raw scores; slots past the compacted count are masked
   if (n_in_chunk < kSlots) {
 #pragma unroll
     for (int a = 0; a < 16; ++a) {
@@ -201,28 +223,27 @@ __device__ __forceinline__ void finish_chunk(const u32x4* buf, f32x16 sc, int n_
       sc[a] = r < n_in_chunk ? sc[a] : -INFINITY;
     }
   }
-  float mx = sc[0];
+  const bool none_yet = st.mref == -INFINITY;
+  bf16x8 pb[2];
+  float rs = chunk_probs(sc, c2, none_yet ? 0.f : st.mref, pb);
+  if (__builtin_amdgcn_ballot_w64(!(rs <= (none_yet ? -1.f : kLazyMax))) != 0) {
+    // the scale c2 > 0 is applied to the maximum (rounding is monotone: max(s) c2 = max(s c2))
+    float mx = sc[0];
 #pragma unroll
-  for (int a = 1; a < 16; ++a) mx = fmaxf(mx, sc[a]);
-  mx = half_swap_max(mx) * c2;
-  // lazy rescale: move the reference only when a score exceeds it by > 2^8 (exact either way)
-  const bool move = mx > st.mref + kRescaleLog2;
-  if (__builtin_amdgcn_ballot_w64(move) != 0) {
-    const float mnew = move ? mx : st.mref;
-    // lanes that keep their reference scale by exactly 1 (also when it is still -inf)
-    const float alpha = move ? fast_exp2(st.mref - mnew) : 1.f;
-    st.l *= alpha;
+    for (int a = 1; a < 16; ++a) mx = fmaxf(mx, sc[a]);
+    mx = half_swap_max(mx) * c2;
+    // lazy rescale: move the reference only when a score exceeds it by > 2^8 (exact either way)
+    const bool move = mx > st.mref + kRescaleLog2;
+    if (__builtin_amdgcn_ballot_w64(move) != 0) {
+      const float mnew = move ? mx : st.mref;
+      // lanes that keep their reference scale by exactly 1 (also when it is still -inf)
+      const float alpha = move ? fast_exp2(st.mref - mnew) : 1.f;
+      st.l *= alpha;
 #pragma unroll
-    for (int d = 0; d < kDBlocks; ++d) o[d] *= alpha;
-    st.mref = mnew;
-  }
-  const float mu = st.mref == -INFINITY ? 0.f : st.mref;
-  float rs = 0.f;
-#pragma unroll
-  for (int a = 0; a < 16; ++a) {
-    const float e = fast_exp2(__builtin_fmaf(sc[a], c2, -mu));
-    sc[a] = e;
-    rs += e;
+      for (int d = 0; d < kDBlocks; ++d) o[d] *= alpha;
+      st.mref = mnew;
+    }
+    rs = chunk_probs(sc, c2, st.mref == -INFINITY ? 0.f : st.mref, pb);
   }
   st.l += rs;
   // transposed reads: lane j of a 16-lane group reads row r0 + 16 s (+ 8) and the 8-byte half
@@ -230,25 +251,19 @@ __device__ __forceinline__ void finish_chunk(const u32x4* buf, f32x16 sc, int n_
   // only in bit 3, which flips bit 1 of lat_key
   const int r0 = 4 * L.h2 + (L.j16 >> 2);
   const int xsub = (L.j16 & 3) >> 1;
-  const int key0 = lat_key(r0);
-  // byte offsets of this lane's two reads for output blocks d with d & 3 = e at k-step 0 (rows r0
-  // and r0 + 8; unit (4 e + 2 dh + xsub) ^ key0, and that unit ^ 2 for row r0 + 8); k-step s and
-  // d >> 2 add the compile-time constant (16 s kLatUnits + 16 (d >> 2)) * 16
-  const int row_b = (r0 * kLatUnits + 32 * L.half) * 16 + (L.j16 & 1) * 8;
+  // byte offsets of this lane's two reads for output blocks d with d & 3 = e at k-step 0: row r0,
+  // unit (4 e + 2 dh + xsub) ^ lat_key(r0), and row r0 + 8, that unit ^ 2.  lat_key(r0) has bits
+  // 2-3 = j16 & 12 and bit 0 = h2; the unit sits in bits 4-7 of the offset and the row, half-row
+  // and 8-byte-half parts in other bits, so the four blocks are one base XOR 64 e, and row r0 + 8
+  // is that XOR 32 plus 8 rows.  k-step s and d >> 2 add the compile-time constant
+  // (16 s kLatUnits + 16 (d >> 2)) * 16
+  const int base_b = (r0 * kLatUnits + 32 * L.half) * 16 + (L.j16 & 1) * 8 + (((2 * L.dh + xsub) ^ L.h2) << 4) +
+                     ((L.j16 & 12) << 4);
   int lo_b[4], hi_b[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    const int u = (4 * e + 2 * L.dh + xsub) ^ key0;
-    lo_b[e] = row_b + u * 16;
-    hi_b[e] = row_b + 8 * kLatUnits * 16 + (u ^ 2) * 16;
-  }
-  bf16x8 pb[2];
-#pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    f32x8 pf;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) pf[e] = sc[8 * s + e];
-    pb[s] = cvt_bf16x8(pf);
+    lo_b[e] = base_b ^ (64 * e);
+    hi_b[e] = (lo_b[e] ^ 32) + 8 * kLatUnits * 16;
   }
   // 16 MFMAs (k-step s = i / 8, output block d = i % 8), fragments read kPvAhead ahead
   const char* bytes = (const char*)buf;
