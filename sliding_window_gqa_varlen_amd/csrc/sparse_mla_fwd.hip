@@ -106,28 +106,35 @@ __device__ __forceinline__ void gather_chunk(const SparseMlaParams& p, const int
   // lane l < 32 reads the index of slot row l once; each transfer takes its rows by readlane
   const int slot = chunk * kSlots + (lane & 31);
   const int my_idx = slot < nv ? s_idx[slot] : t;
+  uint32_t lane16 = (uint32_t)lane * 16u;
+  asm volatile("" : "+v"(lane16));  // kept as one value: each transfer's offset is then one XOR
 #pragma unroll
   for (int i = 0; i < kLatDma; ++i) {
     const int r = i * kWaves + L.wave;  // wave-uniform: a 64-unit block is one latent row
     const uint32_t idx = (uint32_t)__builtin_amdgcn_readlane(my_idx, r);
     u32x4* dst = buf + __builtin_amdgcn_readfirstlane(r * 64);
     // physical unit `lane` of row r holds logical unit (lane & 48) | ((lane & 15) ^ key) = lane ^ key
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(lat, (lds_void*)dst, 16, (uint32_t)((lane ^ lat_key(r)) * 16),
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(lat, (lds_void*)dst, 16, lane16 ^ (uint32_t)(lat_key(r) * 16),
                                              idx * lat_stb, 0, 0);
   }
   if constexpr (DR == 0) return;
   const __amdgpu_buffer_rsrc_t kpe = __builtin_amdgcn_make_buffer_rsrc((void*)p.k_pe, (short)0, -1, kBufferWord3);
   const uint32_t kpe_stb = (uint32_t)p.kpe_st * 2u;
+  // lane part of the rotary offsets: unit (lane >> 2) & 7, 4-byte piece lane & 3 (the unit's
+  // swizzle key is uniform per transfer and enters by XOR)
+  uint32_t rope_lane = (uint32_t)(((lane >> 2) & 7) * 16 + (lane & 3) * 4);
+  asm volatile("" : "+v"(rope_lane));
 #pragma unroll
   for (int i = 0; i < kRopeDma; ++i) {
     const int blk = i * kWaves + L.wave;  // wave-uniform 64-dword block: rows 2 blk and 2 blk + 1
-    const uint32_t i0 = (uint32_t)__builtin_amdgcn_readlane(my_idx, 2 * blk);
-    const uint32_t i1 = (uint32_t)__builtin_amdgcn_readlane(my_idx, 2 * blk + 1);
-    const uint32_t idx = lane < 32 ? i0 : i1;
-    const int unit = ((lane >> 2) & 7) ^ rope_key(2 * blk);  // equal for both rows
+    // both row offsets are uniform (scalar multiplies); each half-wave takes one
+    uint32_t o0 = (uint32_t)__builtin_amdgcn_readlane(my_idx, 2 * blk) * kpe_stb;
+    uint32_t o1 = (uint32_t)__builtin_amdgcn_readlane(my_idx, 2 * blk + 1) * kpe_stb;
+    asm volatile("" : "+s"(o0), "+s"(o1));  // scalar products, not one vector multiply after the select
+    const uint32_t row_off = lane < 32 ? o0 : o1;
     uint32_t* dst = (uint32_t*)(buf + kLatRegion) + __builtin_amdgcn_readfirstlane(blk * 64);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(kpe, (lds_void*)dst, 4,
-                                             idx * kpe_stb + (uint32_t)(unit * 16 + (lane & 3) * 4), 0, 0, 0);
+                                             row_off + (rope_lane ^ (uint32_t)(rope_key(2 * blk) * 16)), 0, 0, 0);
   }
 }
 
@@ -157,20 +164,20 @@ __device__ __forceinline__ f32x16 qk_partial(const u32x4* buf, const bf16x8* qf,
   constexpr int kQFrags = q_frags(DR);
   const Lane L = opaque_lane(Lw);
   f32x16 sc = f32x16{};
-  const int lk = lat_key(L.n);
-  const int rk = rope_key(L.n);
-  int off[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) off[j] = (4 * j + 2 * L.half + L.h2) ^ lk;
-  const int lat_row = L.n * kLatUnits;
-  const int rope_row = kLatRegion + L.n * kRopeUnits;
   // k-step s covers latent units 4s + 2 half + h2 (s < 16), then rotary units 4(s-16) + 2 half + h2;
-  // fragments are read kQAhead MFMAs ahead in a fenced order (the waits count exactly)
+  // fragments are read kQAhead MFMAs ahead in a fenced order (the waits count exactly).
+  // Byte offsets: latent unit (4 j + 2 half + h2) ^ lat_key(n) of row n, where lat_key(n) has bits
+  // 2-3 = 4 (n & 3) and bits 0-1 = (n >> 2) & 3, is one base XOR 64 j (the unit sits in bits 4-7,
+  // the row in bits 10 and up); rotary unit (4 j + 2 half + h2) ^ rope_key(n), j = 0, 1, is one
+  // base XOR 64 j as well (unit in bits 4-6, row in bits 7 and up).
+  const int xh = 2 * L.half + L.h2;
+  const int lat_b = L.n * (kLatUnits * 16) + (L.n & 3) * 64 + ((xh ^ ((L.n >> 2) & 3)) << 4);
+  const int rope_b = (kLatRegion + L.n * kRopeUnits) * 16 + ((xh ^ rope_key(L.n)) << 4);
+  const char* bytes = (const char*)buf;
   u32x4 a[kQFrags];
   auto read = [&](int s) {
-    const int unit = s < 16 ? lat_row + 16 * (s >> 2) + off[s & 3]
-                            : rope_row + ((4 * (s - 16) + 2 * L.half + L.h2) ^ rk);
-    a[s] = buf[unit];
+    const int off = s < 16 ? (lat_b ^ (64 * (s & 3))) + 256 * (s >> 2) : rope_b ^ (64 * (s - 16));
+    a[s] = *(const u32x4*)&bytes[off];
   };
   __builtin_amdgcn_s_setprio(1);  // the wave in its MFMA stream goes first
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)

@@ -185,6 +185,26 @@ def test_scores_growing_along_the_slots(gpu):
     check(out, lse, ref_o, ref_l)
 
 
+@pytest.mark.parametrize("size", [20.0, 200.0])
+def test_score_jump_in_the_middle_of_the_index_rows(gpu, size):
+    """Rotary key rows from position 700 on raise every query's score by `size` (natural-log
+    units; the rotary part enters the scores but not the values).  Ascending index rows meet the
+    jump mid-row, so a chunk's probabilities against the running reference exceed the bound of
+    the path that skips the chunk maximum (for 200, 288 log2 units, they overflow to inf) and
+    that chunk must take the exact path with its maximum."""
+    inp = small(T=1500, topk=512, lengths=[1500], seed=19)
+    kpe = 0.05 * inp["k_pe"]
+    kpe[700:] += size * 24.0 / 64.0  # 64 rotary coordinates, q = 1 there, scale 1/24
+    inp["k_pe"] = W.round_to_bf16(np.ascontiguousarray(kpe, np.float32))
+    q = inp["q"].copy()
+    q[:, :, 512:] = 1.0
+    inp["q"] = W.round_to_bf16(q)
+    ref_o, ref_l = oracle(inp)
+    assert ref_l[1000:].min() > size - 5.0  # the jump dominates the rows that reach it
+    out, lse = run_sparse(inp)
+    check(out, lse, ref_o, ref_l)
+
+
 def test_repeat_runs_are_bitwise_identical(gpu):
     inp = small(400, 128, seed=15)
     o0, l0 = run_sparse(inp)
