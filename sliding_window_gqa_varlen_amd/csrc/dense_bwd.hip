@@ -238,7 +238,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? kDqOcc64 : 2) void bwd_dq_kerne
   const DenseFwdParams& f = p.f;
 
   Tile w;
-  if (!decode_tile(f, w)) return;
+  if (!decode_tile<false>(f, w)) return;
   if (w.padding) {  // tokens outside every document receive no gradient
     const int n_rows = (w.t_end - w.t0) * w.HB;
     for (int idx = threadIdx.x; idx < n_rows * B::U; idx += kThreads) {

@@ -493,7 +493,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? kOcc64 : D == 128 ? 2 : 1) void
   __shared__ u32x4 v1[B::kTileUnits];
 
   Tile w;
-  if (!decode_tile(p, w)) return;
+  if (!decode_tile<true>(p, w)) return;
   if (w.padding) {
     write_padding<__bf16, D>(p, w);
     return;
@@ -650,7 +650,7 @@ __global__ __launch_bounds__(kThreads, 1) void dense_fwd_f32_kernel(DenseFwdPara
   using G = F32Geo<D>;
   __shared__ __attribute__((aligned(16))) float smem[2 * G::kStage];
   Tile w;
-  if (!decode_tile(p, w)) return;
+  if (!decode_tile<true>(p, w)) return;
   if (w.padding) {
     write_padding<float, D>(p, w);
     return;
