@@ -202,6 +202,22 @@ def test_many_documents_both_segment_decodes(gpu, n_docs, D, window):
     assert np.all(out[:7] == 0) and np.all(np.isneginf(lse[:7]))
 
 
+@pytest.mark.parametrize("lengths", [[4096, 1, 0, 2500, 517], [4097, 300, 64]])
+def test_heaviest_first_tile_order_and_its_document_order_fallback(gpu, lengths):
+    """With fewer head chunks than XCDs under a full causal mask the query tiles run heaviest
+    first over all documents when every document has at most 64 key tiles (4096 tokens: 64
+    weight levels, the first case, with an empty and a one-token document and head and tail
+    padding), else in document order (the second case)."""
+    inp = custom(lengths, T=sum(lengths) + 16, Hq=4, Hkv=2, D=64, window=0, dtype="bf16", seed=len(lengths))
+    inp["cu_seqlens"] = inp["cu_seqlens"] + 5  # tokens 0..4 sit before the first document
+    ref_o, ref_l = oracle_full(inp)
+    out, lse = run_dense(inp, "bf16")
+    assert_dense_parity("bf16", out, lse, ref_o, ref_l)
+    end = 5 + sum(lengths)
+    assert np.all(out[:5] == 0) and np.all(out[end:] == 0)
+    assert np.all(np.isneginf(lse[:5])) and np.all(np.isneginf(lse[end:]))
+
+
 @pytest.mark.parametrize("D,window,sinks", [(128, 0, False), (64, 0, True), (128, 300, True), (256, 0, False)])
 def test_scores_growing_along_the_keys(gpu, D, window, sinks):
     """Every query's scores grow by 0.08 to 0.11 per key (5 to 7 per 64-key tile), so the
