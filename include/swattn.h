@@ -121,7 +121,8 @@ typedef struct swa_tensor {
  *   out        [T, Hq, D]  same dtype as q
  *   lse        device f32 [T, Hq] contiguous (natural log), or NULL
  *   stream     hipStream_t
- * Supported: D in {64, 128}, and 256 for bf16. Arithmetic: f32 accumulation; bf16 inputs use bf16
+ * Supported: D in {64, 128}, and 256 for bf16; token strides of k and v and the token and head
+ * strides of out below 2^24 elements (SWA_ERR_UNSUPPORTED otherwise). Arithmetic: f32 accumulation; bf16 inputs use bf16
  * matrix products with the probabilities rounded to bf16 for the value product,
  * and the output is rounded once from f32.
  */
@@ -155,7 +156,8 @@ int32_t varlen_attn_fwd(const swa_tensor* q, const swa_tensor* k, const swa_tens
  *                      library allocates nothing); its contents on return are unspecified
  *   stream             hipStream_t; the dq (which also computes delta), dk/dv and, with
  *                      sinks, two dsink reduction kernels are enqueued in that order
- * Supported: D in {64, 128}, T * Hq < 2^30. Errors: as varlen_attn_fwd; SWA_ERR_NULL when lse,
+ * Supported: D in {64, 128}, T * Hq < 2^30, token strides of q, k, v and dout and the token and
+ * head strides of dq below 2^24 elements. Errors: as varlen_attn_fwd; SWA_ERR_NULL when lse,
  * delta or (with sinks) dsinks is NULL; SWA_ERR_ARG when a gradient aliases an input or
  * another gradient. Arithmetic: bf16 matrix products (P and dS rounded to bf16 as
  * operands), f32 accumulation, one rounding of each gradient.

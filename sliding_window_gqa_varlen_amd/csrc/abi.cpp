@@ -118,6 +118,9 @@ int32_t varlen_attn_fwd(const swa_tensor* q, const swa_tensor* k, const swa_tens
   // per-tile row offsets are computed in 32 bits: 64 rows x token stride must fit
   if (k->stride[0] >= (int64_t)1 << 24 || v->stride[0] >= (int64_t)1 << 24)
     return fail(SWA_ERR_UNSUPPORTED, "k/v token stride must be below 2^24 elements");
+  // the output tile's store offsets are 32-bit byte offsets from the wave's first row
+  if (out->stride[0] >= (int64_t)1 << 24 || out->stride[1] >= (int64_t)1 << 24)
+    return fail(SWA_ERR_UNSUPPORTED, "out token and head strides must be below 2^24 elements");
   if (n_docs < 0) return fail(SWA_ERR_ARG, "n_docs must be >= 0");
   if (window < 0) return fail(SWA_ERR_ARG, "window must be >= 0");
   if (!std::isfinite(scale) || !(scale > 0.f)) return fail(SWA_ERR_ARG, "scale must be finite and > 0");
@@ -192,6 +195,9 @@ int32_t varlen_attn_bwd(const swa_tensor* q, const swa_tensor* k, const swa_tens
   if (T * Hq >= (int64_t)1 << 30) return fail(SWA_ERR_UNSUPPORTED, "T * Hq too large");
   for (const swa_tensor* t : {q, k, v, dout})
     if (t->stride[0] >= (int64_t)1 << 24) return fail(SWA_ERR_UNSUPPORTED, "token strides must be below 2^24 elements");
+  // dq's store offsets are 32-bit byte offsets from the wave's first row
+  if (dq->stride[0] >= (int64_t)1 << 24 || dq->stride[1] >= (int64_t)1 << 24)
+    return fail(SWA_ERR_UNSUPPORTED, "dq token and head strides must be below 2^24 elements");
   if (n_docs < 0) return fail(SWA_ERR_ARG, "n_docs must be >= 0");
   if (window < 0) return fail(SWA_ERR_ARG, "window must be >= 0");
   if (!std::isfinite(scale) || !(scale > 0.f)) return fail(SWA_ERR_ARG, "scale must be finite and > 0");

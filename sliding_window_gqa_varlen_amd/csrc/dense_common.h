@@ -310,19 +310,24 @@ __device__ __forceinline__ void store_out_bf16(void* out, int64_t st, int64_t sh
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's own writes, in order
   // Store k writes column n = k kCols + n0 (n0 = lane / U < kCols).  The bits of n0 and of
   // k kCols do not overlap, so the token (n >> hb_shift) and head (n & (HB - 1)) offsets of n
-  // are sums of a lane part (from n0) and a uniform part (from k): the 64-bit address is
-  // formed once per lane, and each store adds a uniform offset.
+  // are sums of a lane part (from n0) and a uniform part (from k).  The stores are raw buffer
+  // stores from the wave's first (token, head) row: the lane part is a 32-bit byte offset
+  // formed once, the uniform part the scalar offset of each store, so no store needs a 64-bit
+  // address (both parts stay below 2^31 bytes: token and head strides are below 2^24 elements).
   const int u = c.lane % U;
   const int n0 = opaque(c.lane / U);  // the columns n are not shared with the loop's addresses
   const int t_lane = n0 >> hb_shift;
-  __bf16* base = (__bf16*)out + (int64_t)(c.tw0 + t_lane) * st + (int64_t)(w.h0 + (n0 & (w.HB - 1))) * sh + 8 * u;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((__bf16*)out + (int64_t)c.tw0 * st + (int64_t)w.h0 * sh), (short)0, -1, kBufferWord3);
+  const int vlane = ((int)st * t_lane + (int)sh * (n0 & (w.HB - 1)) + 8 * u) * 2;
   const int t_last = c.tw1 - c.tw0 - t_lane;  // uniform token offsets beyond it are past the end
 #pragma unroll
   for (int k = 0; k < 32 / kCols; ++k) {
     const int n = k * kCols + n0;
     const u32x4 val = *(const u32x4*)(img + n * (2 * D) + ((u ^ out_key<D>(n)) << 4));
     const int tk = (k * kCols) >> hb_shift, hk = (k * kCols) & (w.HB - 1);
-    if (tk <= t_last) *(u32x4*)(base + (int64_t)tk * st + (int64_t)hk * sh) = val;
+    if (tk <= t_last)
+      __builtin_amdgcn_raw_buffer_store_b128(val, rs, vlane, __builtin_amdgcn_readfirstlane(((int)st * tk + (int)sh * hk) * 2), 0);
   }
 }
 

@@ -126,6 +126,18 @@ def test_dense_rejects_misaligned_or_strided_layouts(lib):
     assert call_dense(lib, a) == SWA_ERR_LAYOUT
 
 
+@pytest.mark.parametrize("dim", [0, 1])
+def test_dense_rejects_out_strides_beyond_32_bit_store_offsets(lib, dim):
+    """The bf16 output tile leaves by buffer stores whose offsets from the wave's first row are
+    32-bit: token and head strides of out must stay below 2^24 elements (refused before any
+    launch; only the descriptor's stride is changed, no memory is touched)."""
+    a = dense_args()
+    d = {n: describe(a[n]) for n in ("q", "k", "v", "out")}
+    d["out"].stride[dim] = 1 << 24
+    assert call_dense(lib, a, descs=d) == SWA_ERR_UNSUPPORTED
+    assert "out" in lib.swa_last_error().decode()
+
+
 def test_dense_rejects_output_aliasing_an_input(lib):
     a = dense_args(Hq=2, Hkv=2)
     a["out"] = a["q"]
@@ -329,14 +341,24 @@ def bwd_args(T=16, Hq=4, Hkv=2, D=128, dtype=torch.bfloat16):
     return a
 
 
-def call_bwd(lib, a, window=0, scale=0.125, lse="default", delta="default"):
+def call_bwd(lib, a, window=0, scale=0.125, lse="default", delta="default", mutate=None):
     d = {n: describe(a[n]) for n in ("q", "k", "v", "out", "dout", "dq", "dk", "dv")}
+    if mutate is not None:
+        mutate(d)
     ptr = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())  # noqa: E731
     lse_p = ptr(a["lse"]) if lse == "default" else lse
     delta_p = ptr(a["delta"]) if delta == "default" else delta
     return lib.varlen_attn_bwd(*(ctypes.byref(d[n]) for n in ("q", "k", "v", "out", "dout")), lse_p,
                                ptr(a["cu"]), 1, window, scale, ptr(a["sinks"]),
                                *(ctypes.byref(d[n]) for n in ("dq", "dk", "dv")), ptr(a["dsinks"]), delta_p, None)
+
+
+@pytest.mark.parametrize("dim", [0, 1])
+def test_bwd_rejects_dq_strides_beyond_32_bit_store_offsets(lib, dim):
+    def big(d):
+        d["dq"].stride[dim] = 1 << 24
+    assert call_bwd(lib, bwd_args(), mutate=big) == SWA_ERR_UNSUPPORTED
+    assert "dq" in lib.swa_last_error().decode()
 
 
 def test_bwd_rejects_bad_arguments(lib):
