@@ -75,9 +75,10 @@ __device__ __forceinline__ bool item_rank(const DenseFwdParams& p, int x, int j,
 // Virtual tile v of head chunk hc -> the workgroup's query tile; false for idle virtual tiles.
 // `bnd` is this lane's segment boundary bound(lane) when n_docs + 3 <= 64 (else unused).
 __device__ __forceinline__ bool vtile_to_tile(const DenseFwdParams& p, int hc, int v, int bnd, Tile& w) {
-  w.g = hc / p.n_chunks;
+  w.g = p.n_chunks == 1 ? hc : hc / p.n_chunks;  // one chunk per KV head unless G has an odd factor
   const int chunk = hc - w.g * p.n_chunks;
-  const int TQ = p.tile_tokens;
+  const int lg = 7 - p.hb_shift;  // TQ = 128 >> hb_shift tokens per tile: divisions by TQ are shifts
+  const int TQ = 1 << lg;
   // segment s holding virtual tile v: A(s) = floor(bound(s) / TQ) + s, A(s) <= v < A(s+1).
   // A is increasing in s, so the segment is the number of s >= 1 with A(s) <= v: with at
   // most 64 boundaries lane s holds bound(s) and one ballot counts them; otherwise a binary
@@ -94,15 +95,15 @@ __device__ __forceinline__ bool vtile_to_tile(const DenseFwdParams& p, int hc, i
     int hi = p.n_docs + 2;
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
-      if (seg_bound(p, mid) / TQ + mid <= v) lo = mid; else hi = mid;
+      if ((seg_bound(p, mid) >> lg) + mid <= v) lo = mid; else hi = mid;
     }
     seg_start = seg_bound(p, lo);
     seg_end = seg_bound(p, lo + 1);
   }
   w.seg = lo;
   w.seg_start = seg_start;
-  if (seg_start / TQ + lo > v) return false;  // only with decreasing cu_seqlens: no tile
-  w.t0 = w.seg_start + (v - (w.seg_start / TQ + lo)) * TQ;
+  if ((seg_start >> lg) + lo > v) return false;  // only with decreasing cu_seqlens: no tile
+  w.t0 = w.seg_start + (v - ((w.seg_start >> lg) + lo)) * TQ;
   if (w.t0 >= seg_end) return false;
   w.t_end = min(w.t0 + TQ, seg_end);
   w.HB = 1 << p.hb_shift;
@@ -180,7 +181,7 @@ __device__ __forceinline__ int heavy_first_tile(const DenseFwdParams& p, int hc,
     }
     w.padding = true;
   }
-  w.g = hc / p.n_chunks;
+  w.g = p.n_chunks == 1 ? hc : hc / p.n_chunks;
   const int chunk = hc - w.g * p.n_chunks;
   w.seg = seg;
   w.seg_start = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_readlane(bnd, seg));
