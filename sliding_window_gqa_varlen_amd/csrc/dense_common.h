@@ -67,7 +67,7 @@ __device__ __forceinline__ bool item_rank(const DenseFwdParams& p, int x, int j,
   }
   const int L = x * per_xcd + j;
   if (L >= p.n_work) return false;
-  hc = L / VT;
+  hc = (int)(((uint64_t)(uint32_t)L * p.vt_magic) >> p.vt_shift);  // L / VT
   r = L - hc * VT;
   return true;
 }

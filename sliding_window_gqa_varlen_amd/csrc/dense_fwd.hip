@@ -754,6 +754,16 @@ void dense_fwd_plan(DenseFwdParams& p) {
   p.tile_tokens = 128 >> shift;
   p.n_vtiles = p.T / p.tile_tokens + p.n_docs + 2;
   p.n_work = p.Hkv * p.n_chunks * p.n_vtiles;
+  // division by n_vtiles on the device as a multiply and a shift (round-up method for 31-bit
+  // numerators: with l = ceil(log2 d) and m = ceil(2^(31 + l) / d), m d - 2^(31 + l) < 2^l, so
+  // floor(n / d) = floor(n m / 2^(31 + l)) for every 0 <= n < 2^31, and m < 2^32)
+  {
+    const uint64_t d = (uint64_t)(p.n_vtiles > 0 ? p.n_vtiles : 1);
+    int l = 0;
+    while (((uint64_t)1 << l) < d) ++l;
+    p.vt_shift = 31 + l;
+    p.vt_magic = (uint32_t)((((uint64_t)1 << p.vt_shift) + d - 1) / d);
+  }
   p.c2 = p.scale * 1.4426950408889634f;
 }
 

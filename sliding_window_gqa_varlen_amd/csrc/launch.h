@@ -23,6 +23,8 @@ struct DenseFwdParams {
   int32_t tile_tokens;  // tokens per workgroup = 128 >> hb_shift
   int32_t n_vtiles;     // virtual query tiles per (KV head, chunk)
   int32_t n_work;       // Hkv * n_chunks * n_vtiles
+  uint32_t vt_magic;    // floor(L / n_vtiles) = (L * vt_magic) >> vt_shift for 0 <= L < 2^31
+  int32_t vt_shift;
   int32_t window;
   float scale;
   float c2;             // scale * log2(e)
