@@ -200,13 +200,14 @@ __device__ __forceinline__ void softmax_tile(f32x16 (&sc)[2], bool need_mask, in
 // `st.l` holds this half-wave's share of the row sum.  The normaliser comes from v_rcp_f32
 // (within 1 ulp) rather than a correctly rounded division sequence: its error is far below the
 // output's rounding.
+// `sink` is the lane's sink logit (p.sinks[c.hq]) when there are sinks.
 __device__ __forceinline__ float epilogue_scalars(const DenseFwdParams& p, const Tile& w, const Cols& c,
-                                                  const Softmax& st) {
+                                                  const Softmax& st, float sink) {
   const float lt = half_swap_sum(st.l);
   const float m2 = st.mref;  // reference max in log2 units (-inf if nothing was visible)
   float inv, lse_v;
   if (p.sinks != nullptr) {
-    const float s2 = p.sinks[c.hq] * kLog2e;
+    const float s2 = sink * kLog2e;
     const float mm = fmaxf(m2, s2);
     const float corr = fast_exp2(m2 - mm);
     const float lf = lt * corr + fast_exp2(s2 - mm);
@@ -224,7 +225,7 @@ __device__ __forceinline__ float epilogue_scalars(const DenseFwdParams& p, const
 template <typename T, int DB>
 __device__ __forceinline__ void epilogue(const DenseFwdParams& p, const Tile& w, const Cols& c,
                                          const Softmax& st, const f32x16 (&o)[DB]) {
-  const float inv = epilogue_scalars(p, w, c, st);
+  const float inv = epilogue_scalars(p, w, c, st, p.sinks != nullptr ? p.sinks[c.hq] : 0.f);
   if (c.tq < w.t_end) {
     T* ob = (T*)p.out + (int64_t)c.tq * p.o_st + (int64_t)c.hq * p.o_sh;
 #pragma unroll
@@ -500,6 +501,13 @@ __global__ __launch_bounds__(kThreads, D == 64 ? kOcc64 : D == 128 ? 2 : 1) void
   }
   const Cols c = make_cols(p, w);
 
+  // the lane's sink logit, loaded before the Q loads and the first transfers (loads complete in
+  // order, so the transfer waits below cover it): read after the key loop, its latency would
+  // otherwise sit at the end of every workgroup.  Without sinks the load reads q's first element
+  // (always valid memory, never used), so it needs no branch that would make the compiler wait
+  // for it at once.  head_dim 256 has no register to hold it across the loop: it reads the sink
+  // at the end.
+  const float sink = D == 256 ? 0.f : *(p.sinks != nullptr ? p.sinks + c.hq : (const float*)p.q);
   bf16x8 qf[B::kQFrags];
   {
     const __bf16* qb = (const __bf16*)p.q + (int64_t)min(c.tq, w.t_end - 1) * p.q_st + (int64_t)c.hq * p.q_sh;
@@ -626,7 +634,8 @@ __global__ __launch_bounds__(kThreads, D == 64 ? kOcc64 : D == 128 ? 2 : 1) void
   // while the last tile's K may still be read by a wave on its exact path and its V by the PV
   char* img = (char*)(c.wave < 2 ? (last_odd ? k0 : k1) : (last_odd ? v0 : v1)) + (c.wave & 1) * (64 * D);
   const Cols ce = fresh_lane_cols(c, p.hb_shift, w);
-  const float inv = epilogue_scalars(p, w, ce, st);
+  const float inv =
+      epilogue_scalars(p, w, ce, st, D == 256 ? (p.sinks != nullptr ? p.sinks[ce.hq] : 0.f) : sink);
   store_out_bf16<D>(p.out, p.o_st, p.o_sh, w, ce, p.hb_shift, inv, o, img);
 }
 
